@@ -1,0 +1,26 @@
+"""CPU oracle for exact attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import anything from this package.  The GPU library never
+calls it and shares no code with it; the two meet only in the seeded input
+generator (``fa_inputs``), which holds no attention arithmetic.
+
+Contents
+--------
+codecs      decode bf16 bit patterns and OCP E4M3FN codes to float64 from
+            their bit fields; dequantise 64-row block-scaled fp8 tensors.
+attention   the plain definition O = softmax(scale*Q*K^T)*V with its
+            log-sum-exp, in float64, score matrix materialised, two passes
+            (max, then exp/sum); the split-KV partials over key ranges and
+            their log-sum-exp-weighted merge; the elementwise error bound of
+            an fp8-P kernel.
+
+Every function is pinned by ``tests/test_oracle*.py`` against brute force,
+a library routine (torch's float64 scaled-dot-product attention on the CPU)
+and closed-form invariants.  Nothing in here is "parity unpinned".
+"""
+from .codecs import decode_bf16, decode_e4m3fn, dequant_fp8_rows  # noqa: F401
+from .attention import (  # noqa: F401
+    attention, attention_rows, split_bounds, split_partials, merge_partials,
+    decode_attention, fp8_p_error_bound,
+)

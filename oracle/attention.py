@@ -1,0 +1,208 @@
+"""The attention oracle: the plain definition, in float64, on the CPU.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Definition followed (FlashAttention note, "标准注意力的实现问题" and
+"问题分析": S = Q K^T, A = softmax(S / sqrt(d)), O = A V, per (batch, head)
+on (batch, heads, seq_len, head_dim) tensors; the softmax is taken along the
+key axis, after subtracting the row maximum for stability, as in "递归计算
+softmax").  The call's ``scale`` replaces 1/sqrt(d) (the ``softmax_scale``
+argument of the flash_attn_func call shown in "框架集成").
+
+For query row i and key j::
+
+    s_ij  = scale * sum_c q_ic k_jc         (-inf where masked)
+    m_i   = max_j s_ij
+    l_i   = sum_j exp(s_ij - m_i)
+    O_ic  = sum_j exp(s_ij - m_i) / l_i * v_jc
+    LSE_i = m_i + ln l_i                    (natural log)
+
+Causal masking (the ``causal=True`` flag in "使用注意事项"): query i sees key j
+iff j <= i; every configuration has as many queries as keys, so no row is
+ever empty.  A key range with no visible key (only possible for an empty
+split) has LSE = -inf and O = 0.
+
+This file is the definition, evaluated two-pass with the score matrix
+materialised one block of query rows at a time.  It deliberately does not use
+the blocked online recurrence the GPU kernels use; that recurrence appears only
+in the tests, as an invariant checked against this file.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+ROW_BLOCK = 512
+
+
+def _rows(q, k, v, scale, causal, qidx):
+    """O and LSE for query rows ``qidx`` of one (batch, head).
+
+    q: [r, d] the selected query rows; k, v: [Nk, d]; qidx: [r] their indices.
+    """
+    S = scale * (q @ k.T)                                   # [r, Nk] fp64
+    if causal:
+        j = np.arange(k.shape[0])
+        S = np.where(j[None, :] <= qidx[:, None], S, -np.inf)
+    m = S.max(axis=1)                                       # pass 1: row max
+    finite = np.isfinite(m)
+    m_safe = np.where(finite, m, 0.0)
+    E = np.exp(S - m_safe[:, None])                         # pass 2: exp, sum
+    l = E.sum(axis=1)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        P = E / l[:, None]
+    P = np.where(finite[:, None], P, 0.0)
+    O = P @ v
+    lse = np.where(finite, m_safe + np.log(np.where(finite, l, 1.0)), -np.inf)
+    return O, lse
+
+
+def attention(q, k, v, scale, causal=False, row_block=ROW_BLOCK):
+    """Exact attention over the last two axes.
+
+    q: [..., Nq, d]; k, v: [..., Nk, d] (float64 or anything castable).
+    Returns (O [..., Nq, d], LSE [..., Nq]) in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    lead = q.shape[:-2]
+    Nq, d = q.shape[-2:]
+    qf = q.reshape((-1, Nq, d))
+    kf = k.reshape((-1,) + k.shape[-2:])
+    vf = v.reshape((-1,) + v.shape[-2:])
+    O = np.empty(qf.shape[:-1] + (vf.shape[-1],), dtype=np.float64)
+    L = np.empty(qf.shape[:-1], dtype=np.float64)
+    for g in range(qf.shape[0]):
+        for r0 in range(0, Nq, row_block):
+            idx = np.arange(r0, min(r0 + row_block, Nq))
+            O[g, idx], L[g, idx] = _rows(qf[g, idx], kf[g], vf[g], scale, causal, idx)
+    return O.reshape(lead + (Nq, vf.shape[-1])), L.reshape(lead + (Nq,))
+
+
+def attention_rows(q_rows, qidx, k, v, scale, causal=False):
+    """Exact attention for selected query rows of one (batch, head).
+
+    q_rows: [r, d] the query rows; qidx: their row indices (for the mask);
+    k, v: [Nk, d].  Returns (O [r, d], LSE [r]).
+    """
+    return _rows(np.asarray(q_rows, np.float64), np.asarray(k, np.float64),
+                 np.asarray(v, np.float64), scale, causal,
+                 np.asarray(qidx, dtype=np.int64))
+
+
+# ---------------------------------------------------------------------------
+# Split-KV (Flash-Decoding): partial results per key range, then the merge
+# ---------------------------------------------------------------------------
+
+def split_bounds(Lkv: int, num_splits: int):
+    """Key ranges of the splits: chunk = ceil(Lkv/S); split s covers
+    [s*chunk, min((s+1)*chunk, Lkv)), possibly empty at the end."""
+    chunk = -(-Lkv // num_splits)
+    return [(min(s * chunk, Lkv), min((s + 1) * chunk, Lkv)) for s in range(num_splits)]
+
+
+def split_partials(q, k, v, scale, num_splits):
+    """Per-split normalised partial outputs and their log-sum-exps.
+
+    The pages' split example (FlashAttention V2 overview: K and V cut in two,
+    each part giving its own S, A and O, the two O then joined into the final
+    result) generalised to ``num_splits`` key ranges.  Each partial is the
+    exact attention of the queries over that key range alone.
+
+    q: [..., Nq, d]; k, v: [..., Nk, d].  Returns
+    (O_s [..., S, Nq, d], LSE_s [..., S, Nq]); an empty range gives O_s = 0,
+    LSE_s = -inf.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    outs, lses = [], []
+    for lo, hi in split_bounds(k.shape[-2], num_splits):
+        if hi > lo:
+            o, l = attention(q, k[..., lo:hi, :], v[..., lo:hi, :], scale, causal=False)
+        else:
+            o = np.zeros(q.shape[:-1] + (v.shape[-1],))
+            l = np.full(q.shape[:-1], -np.inf)
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs, axis=-3), np.stack(lses, axis=-2)
+
+
+def merge_partials(O_s, LSE_s):
+    """Merge split partials: M = max_s LSE_s, w_s = exp(LSE_s - M),
+    O = sum_s w_s O_s / sum_s w_s, LSE = M + ln sum_s w_s.
+
+    O_s: [..., S, Nq, d]; LSE_s: [..., S, Nq].  All -inf -> O = 0, LSE = -inf.
+    """
+    O_s = np.asarray(O_s, np.float64)
+    LSE_s = np.asarray(LSE_s, np.float64)
+    M = LSE_s.max(axis=-2)
+    finite = np.isfinite(M)
+    Ms = np.where(finite, M, 0.0)
+    w = np.where(np.isfinite(LSE_s), np.exp(LSE_s - Ms[..., None, :]), 0.0)
+    W = w.sum(axis=-2)
+    Wsafe = np.where(finite, W, 1.0)
+    O = (w[..., None] * O_s).sum(axis=-3) / Wsafe[..., None]
+    O = np.where(finite[..., None], O, 0.0)
+    LSE = np.where(finite, Ms + np.log(Wsafe), -np.inf)
+    return O, LSE
+
+
+def decode_attention(q, k, v, scale):
+    """Single-query decode: exact, unmasked attention of q [..., 1, d] over the
+    whole cache k, v [..., Lkv, d].  Splitting the keys does not change the
+    result, so the reference for the split-KV path is the unsplit definition."""
+    return attention(q, k, v, scale, causal=False)
+
+
+# ---------------------------------------------------------------------------
+# fp8: the elementwise bound on an fp8-P kernel's error
+# ---------------------------------------------------------------------------
+
+def fp8_p_error_bound(q, k, v, scale, causal, p_prescale, qidx=None):
+    """Elementwise bound |O_kernel - O| <= B for a kernel that rounds the
+    unnormalised probabilities to E4M3FN before the P*V product.
+
+    q, k, v are the *dequantised* inputs of one (batch, head): q [r, d] (rows
+    ``qidx``), k, v [Nk, d].  With p_ij = exp(s_ij - m_i) / l_i the exact
+    probabilities, a kernel storing sigma*exp(s - m') for some running max
+    m' <= m_i in E4M3FN makes an error per weight of at most 2^-4 relative
+    (3 mantissa bits, half an ulp) or 2^-10/sigma absolute (half the subnormal
+    quantum 2^-9, undone by the pre-scale sigma).  Rescaling by
+    exp(m' - m_i) <= 1 only shrinks the absolute part.  Whether the kernel
+    divides by the unrounded sum or by the sum of the rounded weights, the
+    output error is at most sum_j |dp_j| (|v_jc| + |O_ic|) / (l_i (1 - 2^-4)),
+    hence the 16/15.  bf16 rounding of the output adds 2^-8 |O_ic|, and
+    1e-4 covers float32 accumulation.
+
+    Returns (O [r, d], LSE [r], B [r, d]).
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    r = q.shape[0]
+    if qidx is None:
+        qidx = np.arange(r)
+    qidx = np.asarray(qidx, np.int64)
+    S = scale * (q @ k.T)
+    if causal:
+        j = np.arange(k.shape[0])
+        visible = j[None, :] <= qidx[:, None]
+        S = np.where(visible, S, -np.inf)
+    else:
+        visible = np.ones(S.shape, dtype=bool)
+    m = S.max(axis=1)
+    E = np.exp(S - m[:, None])
+    l = E.sum(axis=1)
+    P = E / l[:, None]
+    O = P @ v
+    lse = m + np.log(l)
+    absv = np.abs(v)
+    absO = np.abs(O)
+    n_vis = visible.sum(axis=1).astype(np.float64)
+    # sum_j P_ij (|v_jc| + |O_ic|)   and   sum_{visible j} (|v_jc| + |O_ic|) / l_i
+    rel_term = P @ absv + absO
+    abs_term = (visible.astype(np.float64) @ absv + n_vis[:, None] * absO) / l[:, None]
+    Bnd = (16.0 / 15.0) * (2.0 ** -4 * rel_term + 2.0 ** -10 / p_prescale * abs_term) \
+        + 2.0 ** -8 * absO + 1e-4
+    return O, lse, Bnd

@@ -1,0 +1,333 @@
+"""Pins for the attention oracle (CPU only).
+
+The oracle is the plain definition; these tests tie it to things other than
+itself: hand-worked cases, brute force in scalar Python, torch's float64 CPU
+attention (a library routine that also returns the log-sum-exp), the blocked
+online recurrence of the pages, and closed-form invariants.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import attention, attention_rows, merge_partials, split_partials
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+# ---------------------------------------------------------------------------
+# hand-worked cases
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", json.load(open(GOLDEN))["cases"], ids=lambda c: c["name"])
+def test_hand_worked(case):
+    q, k, v = (np.array(case[n], dtype=np.float64) for n in ("q", "k", "v"))
+    O, L = attention(q, k, v, case["scale"], case["causal"])
+    np.testing.assert_allclose(O, case["O"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L, case["LSE"], rtol=0, atol=1e-12)
+    if "num_splits" in case:
+        Os, Ls = split_partials(q, k, v, case["scale"], case["num_splits"])
+        np.testing.assert_allclose(Os, case["O_split"], atol=1e-12)
+        np.testing.assert_allclose(Ls, case["LSE_split"], atol=1e-12)
+        Om, Lm = merge_partials(Os, Ls)
+        np.testing.assert_allclose(Om, case["O"], atol=1e-12)
+        np.testing.assert_allclose(Lm, case["LSE"], atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# brute force: scalar Python, no max subtraction, exact summation
+# ---------------------------------------------------------------------------
+
+def _brute(q, k, v, scale, causal):
+    Nq, d = len(q), len(q[0])
+    O, L = [], []
+    for i in range(Nq):
+        ws = []
+        for j in range(len(k)):
+            if causal and j > i:
+                continue
+            s = scale * math.fsum(q[i][c] * k[j][c] for c in range(d))
+            ws.append((math.exp(s), j))
+        tot = math.fsum(w for w, _ in ws)
+        O.append([math.fsum(w * v[j][c] for w, j in ws) / tot for c in range(len(v[0]))])
+        L.append(math.log(tot))
+    return np.array(O), np.array(L)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,d", [(1, 1), (3, 2), (5, 4), (8, 3)])
+def test_brute_force(N, d, causal):
+    rng = np.random.default_rng(1000 + 10 * N + d + causal)
+    q, k, v = _rand(rng, N, d), _rand(rng, N, d), _rand(rng, N, d + 1)
+    scale = 0.7
+    O, L = attention(q, k, v, scale, causal)
+    Ob, Lb = _brute(q.tolist(), k.tolist(), v.tolist(), scale, causal)
+    np.testing.assert_allclose(O, Ob, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(L, Lb, rtol=1e-12, atol=1e-12)
+
+
+def test_brute_force_rectangular():
+    rng = np.random.default_rng(7)
+    q, k, v = _rand(rng, 3, 4), _rand(rng, 6, 4), _rand(rng, 6, 2)
+    O, L = attention(q, k, v, 0.5)
+    Ob, Lb = _brute(q.tolist(), k.tolist(), v.tolist(), 0.5, False)
+    np.testing.assert_allclose(O, Ob, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(L, Lb, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# library routine: torch's float64 CPU flash attention (returns O and LSE)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 1, 128, 64), (2, 3, 67, 128), (1, 2, 300, 16)])
+def test_against_torch_cpu(shape, causal):
+    rng = np.random.default_rng(sum(shape) + causal)
+    q, k, v = (_rand(rng, *shape) for _ in range(3))
+    scale = 1.0 / math.sqrt(shape[-1])
+    O, L = attention(q, k, v, scale, causal, row_block=50)
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    to, tl = torch.ops.aten._scaled_dot_product_flash_attention_for_cpu(
+        tq, tk, tv, 0.0, causal, scale=scale)[:2]
+    np.testing.assert_allclose(O, to.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(L, tl.numpy(), rtol=1e-10, atol=1e-12)
+    ts = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)
+    np.testing.assert_allclose(O, ts.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_attention_rows_matches_full():
+    rng = np.random.default_rng(3)
+    q, k, v = _rand(rng, 40, 8), _rand(rng, 40, 8), _rand(rng, 40, 8)
+    O, L = attention(q, k, v, 0.3, True)
+    idx = np.array([0, 1, 17, 39])
+    Or, Lr = attention_rows(q[idx], idx, k, v, 0.3, True)
+    np.testing.assert_allclose(Or, O[idx], rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(Lr, L[idx], rtol=1e-14, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# I1: the pages' blocked online recurrence reaches the two-pass result
+# ---------------------------------------------------------------------------
+
+def _online(q, k, v, scale, causal, bc):
+    """Per query row, walk the keys in blocks of ``bc``: m_new = max(m_old,
+    rowmax), l_new = l_old*e^(m_old-m_new) + sum_j e^(s_j-m_new),
+    O_new = O_old*e^(m_old-m_new) + sum_j e^(s_j-m_new) v_j; O/l at the end."""
+    Nq, Nk = q.shape[0], k.shape[0]
+    O = np.zeros((Nq, v.shape[1]))
+    L = np.zeros(Nq)
+    for i in range(Nq):
+        m, l, acc = -np.inf, 0.0, np.zeros(v.shape[1])
+        hi = i + 1 if causal else Nk
+        for j0 in range(0, hi, bc):
+            j1 = min(j0 + bc, hi)
+            s = scale * (k[j0:j1] @ q[i])
+            m_new = max(m, s.max())
+            f = math.exp(m - m_new) if np.isfinite(m) else 0.0
+            p = np.exp(s - m_new)
+            l = l * f + p.sum()
+            acc = acc * f + p @ v[j0:j1]
+            m = m_new
+        O[i] = acc / l
+        L[i] = m + math.log(l)
+    return O, L
+
+
+@pytest.mark.parametrize("bc", [1, 3, 16, 64])
+@pytest.mark.parametrize("causal", [False, True])
+def test_online_recurrence_equals_two_pass(bc, causal):
+    rng = np.random.default_rng(bc * 2 + causal)
+    q, k, v = _rand(rng, 50, 16) * 3, _rand(rng, 50, 16) * 3, _rand(rng, 50, 16)
+    O, L = attention(q, k, v, 0.25, causal)
+    Oo, Lo = _online(q, k, v, 0.25, causal, bc)
+    np.testing.assert_allclose(Oo, O, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(Lo, L, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# closed forms and invariants
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_weights_sum_to_one(causal):
+    # I2: sum_j exp(s_ij - LSE_i) = 1 over the visible keys
+    rng = np.random.default_rng(11)
+    q, k, v = _rand(rng, 33, 8), _rand(rng, 33, 8), _rand(rng, 33, 8)
+    _, L = attention(q, k, v, 0.4, causal)
+    S = 0.4 * q @ k.T
+    vis = np.tril(np.ones((33, 33), bool)) if causal else np.ones((33, 33), bool)
+    tot = np.where(vis, np.exp(S - L[:, None]), 0.0).sum(axis=1)
+    np.testing.assert_allclose(tot, 1.0, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_value_rows(causal):
+    # I3: every V row equal to c  =>  every output row equals c
+    rng = np.random.default_rng(12)
+    q, k = _rand(rng, 20, 8) * 4, _rand(rng, 20, 8) * 4
+    c = _rand(rng, 5)
+    O, _ = attention(q, k, np.tile(c, (20, 1)), 0.5, causal)
+    np.testing.assert_allclose(O, np.tile(c, (20, 1)), atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_keys(causal):
+    # I4: all keys equal => O_i = mean of the visible V rows, LSE_i = scale q_i.k + ln n_i
+    rng = np.random.default_rng(13)
+    N = 17
+    q, kk, v = _rand(rng, N, 6), _rand(rng, 6), _rand(rng, N, 3)
+    O, L = attention(q, np.tile(kk, (N, 1)), v, 0.9, causal)
+    n = np.arange(1, N + 1) if causal else np.full(N, N)
+    mean = np.cumsum(v, axis=0) / n[:, None] if causal else np.tile(v.mean(0), (N, 1))
+    np.testing.assert_allclose(O, mean, atol=1e-13)
+    np.testing.assert_allclose(L, 0.9 * q @ kk + np.log(n), atol=1e-13)
+
+
+def test_causal_first_row():
+    # I6: row 0 sees only key 0
+    rng = np.random.default_rng(14)
+    q, k, v = _rand(rng, 9, 5), _rand(rng, 9, 5), _rand(rng, 9, 5)
+    O, L = attention(q, k, v, 0.6, True)
+    np.testing.assert_array_equal(O[0], v[0])
+    assert L[0] == pytest.approx(0.6 * q[0] @ k[0], abs=1e-15)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_query_uniform(causal):
+    # I7: q = 0 => uniform weights
+    rng = np.random.default_rng(15)
+    N = 12
+    k, v = _rand(rng, N, 4), _rand(rng, N, 4)
+    O, L = attention(np.zeros((N, 4)), k, v, 1.0, causal)
+    n = np.arange(1, N + 1) if causal else np.full(N, N)
+    mean = np.cumsum(v, axis=0) / n[:, None] if causal else np.tile(v.mean(0), (N, 1))
+    np.testing.assert_allclose(O, mean, atol=1e-14)
+    np.testing.assert_allclose(L, np.log(n), atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_shift(causal):
+    # I8: K' = K + 1 u^T leaves O unchanged and adds scale q.u to LSE
+    rng = np.random.default_rng(16)
+    q, k, v, u = _rand(rng, 15, 4), _rand(rng, 15, 4), _rand(rng, 15, 4), _rand(rng, 4)
+    O, L = attention(q, k, v, 0.5, causal)
+    O2, L2 = attention(q, k + u[None, :], v, 0.5, causal)
+    np.testing.assert_allclose(O2, O, atol=1e-13)
+    np.testing.assert_allclose(L2, L + 0.5 * q @ u, atol=1e-13)
+
+
+def test_permutation_and_linearity():
+    # I9: non-causal output ignores a joint permutation of K/V rows; linear in V
+    rng = np.random.default_rng(17)
+    q, k, v, w = (_rand(rng, 21, 6) for _ in range(4))
+    O, L = attention(q, k, v, 0.5)
+    perm = rng.permutation(21)
+    O2, L2 = attention(q, k[perm], v[perm], 0.5)
+    np.testing.assert_allclose(O2, O, atol=1e-13)
+    np.testing.assert_allclose(L2, L, atol=1e-13)
+    Ow, _ = attention(q, k, w, 0.5)
+    O3, _ = attention(q, k, 2.0 * v - 3.0 * w, 0.5)
+    np.testing.assert_allclose(O3, 2.0 * O - 3.0 * Ow, atol=1e-12)
+
+
+def test_large_scores_stable():
+    # I10: scores of order 1e3 stay finite and pick the argmax key's value row
+    rng = np.random.default_rng(18)
+    q, k, v = _rand(rng, 10, 8) * 100, _rand(rng, 10, 8), _rand(rng, 10, 8)
+    O, L = attention(q, k, v, 1.0)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
+    S = q @ k.T
+    top2 = np.sort(S, axis=1)[:, -2:]
+    sure = (top2[:, 1] - top2[:, 0]) > 40  # the runner-up weight is below e^-40
+    assert sure.any()
+    np.testing.assert_allclose(O[sure], v[S.argmax(axis=1)][sure], atol=1e-12)
+    np.testing.assert_allclose(L, S.max(axis=1) + np.log(np.exp(S - S.max(1, keepdims=True)).sum(1)))
+
+
+# ---------------------------------------------------------------------------
+# I5: split-KV partials and their merge
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("Lkv,S", [(64, 1), (64, 2), (100, 3), (1024, 64), (70, 64), (5, 4)])
+def test_split_merge_equals_unsplit(Lkv, S):
+    rng = np.random.default_rng(Lkv + S)
+    q, k, v = _rand(rng, 2, 1, 32), _rand(rng, 2, Lkv, 32) * 2, _rand(rng, 2, Lkv, 32)
+    O, L = oracle.decode_attention(q, k, v, 0.2)
+    Os, Ls = split_partials(q, k, v, 0.2, S)
+    assert Os.shape == (2, S, 1, 32) and Ls.shape == (2, S, 1)
+    Om, Lm = merge_partials(Os, Ls)
+    np.testing.assert_allclose(Om, O, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(Lm, L, rtol=1e-12, atol=1e-13)
+    # each partial is attention over its own key range alone
+    for s, (lo, hi) in enumerate(oracle.split_bounds(Lkv, S)):
+        if hi > lo:
+            o, l = attention(q, k[:, lo:hi], v[:, lo:hi], 0.2)
+            np.testing.assert_allclose(Os[:, s], o, atol=1e-14)
+        else:
+            assert np.all(Ls[:, s] == -np.inf) and np.all(Os[:, s] == 0)
+
+
+def test_split_bounds():
+    assert oracle.split_bounds(65536, 64)[0] == (0, 1024)
+    assert oracle.split_bounds(65536, 64)[-1] == (64512, 65536)
+    b = oracle.split_bounds(70, 64)   # chunk 2 -> 35 non-empty splits
+    assert b[34] == (68, 70) and b[35] == (70, 70) and b[-1] == (70, 70)
+    assert oracle.split_bounds(7, 7) == [(i, i + 1) for i in range(7)]
+
+
+def test_merge_all_empty():
+    Om, Lm = merge_partials(np.zeros((3, 1, 4)), np.full((3, 1), -np.inf))
+    assert np.all(Om == 0) and np.all(Lm == -np.inf)
+
+
+# ---------------------------------------------------------------------------
+# the fp8-P error bound
+# ---------------------------------------------------------------------------
+
+def _sim_fp8_p(q, k, v, scale, causal, sigma, bc, normalise_by_rounded):
+    """Blocked online softmax with the unnormalised P rounded to E4M3FN
+    (times the pre-scale sigma) before the P*V product."""
+    from fa_inputs import f64_to_e4m3fn_codes
+    Nq, Nk = q.shape[0], k.shape[0]
+    O = np.zeros((Nq, v.shape[1]))
+    for i in range(Nq):
+        m, l, acc = -np.inf, 0.0, np.zeros(v.shape[1])
+        hi = i + 1 if causal else Nk
+        for j0 in range(0, hi, bc):
+            j1 = min(j0 + bc, hi)
+            s = scale * (k[j0:j1] @ q[i])
+            m_new = max(m, s.max())
+            f = math.exp(m - m_new) if np.isfinite(m) else 0.0
+            p = np.exp(s - m_new)
+            ph = oracle.decode_e4m3fn(f64_to_e4m3fn_codes(p * sigma)) / sigma
+            l = l * f + (ph.sum() if normalise_by_rounded else p.sum())
+            acc = acc * f + ph @ v[j0:j1]
+            m = m_new
+        O[i] = acc / l
+    return O
+
+
+@pytest.mark.parametrize("rounded", [False, True])
+@pytest.mark.parametrize("sigma", [1.0, 256.0])
+def test_fp8_bound_holds_and_is_tight(rounded, sigma):
+    rng = np.random.default_rng(19)
+    N = 96
+    q, k, v = _rand(rng, N, 16) * 2, _rand(rng, N, 16) * 2, _rand(rng, N, 16)
+    v[rng.random(v.shape) < 0.02] *= 20
+    O, L, Bnd = oracle.fp8_p_error_bound(q, k, v, 0.25, True, sigma)
+    Oref, Lref = attention(q, k, v, 0.25, True)
+    np.testing.assert_allclose(O, Oref, atol=1e-13)
+    np.testing.assert_allclose(L, Lref, atol=1e-13)
+    Osim = _sim_fp8_p(q, k, v, 0.25, True, sigma, 16, rounded)
+    err = np.abs(Osim - O)
+    assert np.all(err <= Bnd)
+    # tight to within a small factor somewhere (the bound is not vacuous)
+    assert np.max(err / Bnd) > 0.05
