@@ -1,0 +1,291 @@
+#!/usr/bin/env python
+"""Throughput of the attention library on one MI355X.
+
+One step = one pass of the whole hot path over resident synthetic inputs:
+  * bf16 forward, B=2 H=32 N=2048 d=128, causal and non-causal
+  * bf16 forward, B=1 H=16 N=16384 d=128, causal
+  * split-KV decode, B=8 H=32 Lkv=65536 d=128, 64 splits (split + merge kernels)
+  * fp8 forward, B=4 H=16 N=8192 d=128, causal (when the library has it)
+
+``value`` is the bf16 causal forward throughput over the N=2048 and N=16384
+workloads (their FLOPs over their summed kernel time, 4*B*H*N^2*d/2 per
+causal call); the decode bandwidth is reported beside it.  Each launch is
+bracketed by HIP events on the stream it runs on.  The CPU oracle is timed on
+a bounded sample of the same workloads (rank 0, N=1 only).
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd TFLOPS (bf16 causal, N=2K-16K) + split-KV decode HBM GB/s, 1 GPU"
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk)
+PEAK_FP8_TFLOPS = 5033.2      # dense fp8
+PEAK_HBM_GBS = 8000.0
+
+
+def fwd_flops(w, causal):
+    f = 4.0 * w.B * w.H * w.N * w.N * w.d
+    return f / 2 if causal else f
+
+
+def fwd_bytes(w, in_bytes=2, out_bytes=2):
+    n = w.B * w.H * w.N * w.d
+    return 3 * n * in_bytes + n * out_bytes + w.B * w.H * w.N * 4
+
+
+def decode_bytes(w):
+    kv = 2 * w.B * w.H * w.Lkv * w.d * 2
+    return kv + 2 * w.B * w.H * w.d * 2
+
+
+def cpu_info():
+    model = platform.processor() or ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model
+
+
+def cpu_baseline(seconds):
+    """Time the fp64 oracle on a bounded sample of the forward and decode workloads."""
+    import numpy as np
+    import fa_inputs as fi
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    w = fi.WORKLOADS[2]
+    t0 = time.perf_counter()
+    flops, heads = 0.0, 0
+    while time.perf_counter() - t0 < seconds * 0.75 or heads == 0:
+        b, h = divmod(heads % (w.B * w.H), w.H)
+        q, k, v = (oracle.decode_bf16(fi.bf16_slice(w.wid, t, b, h, w.N, w.d)) for t in range(3))
+        oracle.attention(q, k, v, w.scale, True)
+        flops += 4.0 * w.N * w.N * w.d / 2
+        heads += 1
+    t_fwd = time.perf_counter() - t0
+    # decode: only the oracle call is timed (generation excluded), (b,h) pairs
+    # until about a quarter of the budget is spent
+    wd = fi.WORKLOADS[4]
+    t_dec, nbytes, pairs = 0.0, 0, 0
+    while t_dec < seconds * 0.25 or pairs == 0:
+        b, h = divmod(pairs % (wd.B * wd.H), wd.H)
+        qb = fi.bf16_slice(wd.wid, 0, b, h, 1, wd.d)
+        kb = fi.bf16_slice(wd.wid, 1, b, h, wd.Lkv, wd.d)
+        vb = fi.bf16_slice(wd.wid, 2, b, h, wd.Lkv, wd.d)
+        ts = time.perf_counter()
+        oracle.decode_attention(*(oracle.decode_bf16(x) for x in (qb, kb, vb)), wd.scale)
+        t_dec += time.perf_counter() - ts
+        nbytes += kb.nbytes + vb.nbytes
+        pairs += 1
+    return {
+        "value": flops / t_fwd / 1e12,
+        "unit": "TFLOPS",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"fp64 two-pass oracle, causal B=2 H=32 N=2048 d=128: {heads} of 64 heads "
+                   f"in {t_fwd:.1f} s (input generation and bf16 decoding included); "
+                   f"decode oracle B=8 H=32 Lkv=65536 d=128: {pairs} (b,h) pairs in {t_dec:.1f} s"),
+        "decode_value": nbytes / t_dec / 1e9,
+        "decode_unit": "GB/s",
+        "cpu_model": cpu_info(),
+        "affinity_cores": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--only", default="all", help="all | c2c | c2n | c3 | c4 | c5 (profiling)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy per step (for HBM counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_attention_116_amd as fa
+    import fa_inputs as fi
+
+    torch.cuda.set_device(0)
+    fa.load()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def up_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    jobs = []   # (name, launch-fn, flops, bytes, kind)
+    want = (lambda n: args.only in ("all", n))
+
+    w2, w3, w4, w5 = (fi.WORKLOADS[i] for i in (2, 3, 4, 5))
+    if want("c2c") or want("c2n"):
+        q2, k2, v2 = (up_bf16(fi.bf16_tensor(w2.wid, t, w2.B, w2.H, w2.N, w2.d)) for t in range(3))
+        o2 = torch.empty_like(q2)
+        l2 = torch.empty((w2.B, w2.H, w2.N), dtype=torch.float32, device=dev)
+        for causal, tag in ((True, "c2c"), (False, "c2n")):
+            if want(tag):
+                jobs.append((tag, (lambda c=causal: fa.fa_fwd_ex(
+                    q2, k2, v2, o2, l2, w2.B, w2.H, w2.N, w2.d, w2.scale, c, stream=stream)),
+                    fwd_flops(w2, causal), fwd_bytes(w2), "fwd_bf16"))
+    if want("c3"):
+        q3, k3, v3 = (up_bf16(fi.bf16_tensor(w3.wid, t, w3.B, w3.H, w3.N, w3.d)) for t in range(3))
+        o3 = torch.empty_like(q3)
+        l3 = torch.empty((w3.B, w3.H, w3.N), dtype=torch.float32, device=dev)
+        jobs.append(("c3", lambda: fa.fa_fwd_ex(q3, k3, v3, o3, l3, w3.B, w3.H, w3.N, w3.d,
+                                                w3.scale, True, stream=stream),
+                     fwd_flops(w3, True), fwd_bytes(w3), "fwd_bf16"))
+    if want("c4"):
+        q4 = up_bf16(fi.bf16_tensor(w4.wid, 0, w4.B, w4.H, 1, w4.d))
+        k4 = up_bf16(fi.bf16_tensor(w4.wid, 1, w4.B, w4.H, w4.Lkv, w4.d))
+        v4 = up_bf16(fi.bf16_tensor(w4.wid, 2, w4.B, w4.H, w4.Lkv, w4.d))
+        o4 = torch.empty_like(q4)
+        l4 = torch.empty((w4.B, w4.H), dtype=torch.float32, device=dev)
+        wsb = fa.fa_decode_workspace_bytes(w4.B, w4.H, w4.d, w4.num_splits)
+        ws4 = torch.empty(wsb // 4, dtype=torch.float32, device=dev)
+        jobs.append(("c4", lambda: fa.fa_decode_splitkv_ex(
+            q4, k4, v4, o4, l4, w4.B, w4.H, w4.Lkv, w4.d, w4.num_splits, w4.scale, ws4, wsb,
+            stream=stream), 4.0 * w4.B * w4.H * w4.Lkv * w4.d, decode_bytes(w4), "decode"))
+    def fp8_built():
+        t = torch.zeros((1, 1, 64, 128), dtype=torch.uint8, device=dev)
+        sc = torch.ones((1, 1, 1), dtype=torch.float32, device=dev)
+        ob = torch.empty((1, 1, 64, 128), dtype=torch.bfloat16, device=dev)
+        lb = torch.empty((1, 1, 64), dtype=torch.float32, device=dev)
+        try:
+            fa.fa_fwd_ex(t, t, t, ob, lb, 1, 1, 64, 128, 0.1, True, in_dtype=fa.FA_FP8_E4M3,
+                         q_scale=sc, k_scale=sc, v_scale=sc, stream=stream)
+            return True
+        except fa.FaError as e:
+            if e.status != fa.FA_ERR_UNSUPPORTED:
+                raise
+            return False
+
+    if want("c5") and fp8_built():
+        if True:
+            x = {}
+            for n, t in (("q", 0), ("k", 1), ("v", 2)):
+                c, s = fi.fp8_tensor(w5.wid, t, w5.B, w5.H, w5.N, w5.d)
+                x[n] = torch.from_numpy(c).to(dev)
+                x[n + "s"] = torch.from_numpy(s).to(dev)
+            o5 = torch.empty((w5.B, w5.H, w5.N, w5.d), dtype=torch.bfloat16, device=dev)
+            l5 = torch.empty((w5.B, w5.H, w5.N), dtype=torch.float32, device=dev)
+
+            def run5():
+                fa.fa_fwd_ex(x["q"], x["k"], x["v"], o5, l5, w5.B, w5.H, w5.N, w5.d, w5.scale,
+                             True, in_dtype=fa.FA_FP8_E4M3, q_scale=x["qs"], k_scale=x["ks"],
+                             v_scale=x["vs"], stream=stream)
+            run5()
+            torch.cuda.synchronize()
+            n5 = w5.B * w5.H * w5.N
+            jobs.append(("c5", run5, fwd_flops(w5, True),
+                         3 * n5 * w5.d + 3 * n5 // 64 * 4 + n5 * w5.d * 2 + n5 * 4, "fwd_fp8"))
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        jobs.append(("copy_1GiB", lambda: dst.copy_(src), 0.0, 2 * src.numel() * 4, "copy"))
+
+    def step(evs=None):
+        for i, (_, fn, _, _, _) in enumerate(jobs):
+            if evs is not None:
+                evs[i][0].record(stream)
+            fn()
+            if evs is not None:
+                evs[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in jobs] for _ in range(args.steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_all0.record(stream)
+    for s in range(args.steps):
+        step(evs[s])
+    t_all1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_all0.elapsed_time(t_all1) / args.steps
+
+    res = {}
+    for i, (name, _, flops, nbytes, kind) in enumerate(jobs):
+        ts = np.array([evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)])
+        res[name] = {"kind": kind, "ms_mean": float(ts.mean()), "ms_median": float(np.median(ts)),
+                     "ms_min": float(ts.min()), "flops": flops, "bytes": nbytes}
+        if kind.startswith("fwd"):
+            res[name]["tflops"] = flops / (ts.mean() * 1e-3) / 1e12
+        else:
+            res[name]["gbs"] = nbytes / (ts.mean() * 1e-3) / 1e9
+
+    causal = [n for n in ("c2c", "c3") if n in res]
+    value = None
+    if causal:
+        value = sum(res[n]["flops"] for n in causal) / (
+            sum(res[n]["ms_mean"] for n in causal) * 1e-3) / 1e12
+    dom = "c3" if "c3" in res else (causal[0] if causal else next(iter(res), None))
+    roof = None
+    if dom and res[dom]["kind"].startswith("fwd"):
+        pk = PEAK_FP8_TFLOPS if res[dom]["kind"] == "fwd_fp8" else PEAK_BF16_TFLOPS
+        a = res[dom]["tflops"]
+        roof = {"kernel": f"fa_fwd_bf16_kernel ({dom})", "bound": "mfma", "achieved": a,
+                "peak": pk, "unit": "TFLOP/s", "frac": a / pk, "traffic": None}
+    decode = None
+    if "c4" in res:
+        g = res["c4"]["gbs"]
+        decode = {"value": g, "unit": "GB/s", "ms": res["c4"]["ms_mean"],
+                  "roofline": {"kernel": "fa_decode_split_kernel + fa_decode_combine_kernel",
+                               "bound": "hbm", "achieved": g, "peak": PEAK_HBM_GBS,
+                               "unit": "GB/s", "frac": g / PEAK_HBM_GBS, "traffic": None}}
+    prop = torch.cuda.get_device_properties(0)
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "bf16 causal fwd B2H32N2048d128 + B1H16N16384d128 "
+                               "(value); split-KV decode B8H32Lkv65536d128 S64 (decode)",
+                   "only": args.only},
+        "roofline": roof,
+        "decode": decode,
+        "workloads": res,
+        "device": {"name": prop.name, "cus": prop.multi_processor_count,
+                   "gcn_arch": getattr(prop, "gcnArchName", "")},
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline and args.only == "all":
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

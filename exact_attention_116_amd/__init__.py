@@ -1,0 +1,129 @@
+"""Exact attention on AMD Instinct MI355X: Python binding of ``libfa.so``.
+
+The functions below have the names and arguments of the C entry points in
+``include/fa.h`` and only marshal arguments (device pointers from tensors or
+integers, sizes, the stream handle).  Every step of the computation runs in
+the library's HIP kernels; when the library is missing, ``load()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
+FA_BF16, FA_FP32, FA_FP8_E4M3 = range(3)
+
+EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_decode_splitkv", "fa_decode_workspace_bytes",
+           "fa_decode_splitkv_ex", "fa_status_string", "fa_last_error")
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class fa_fwd_params(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("q_scale", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p),
+                ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+                ("B", ctypes.c_int), ("H", ctypes.c_int), ("N", ctypes.c_int), ("d", ctypes.c_int),
+                ("scale", ctypes.c_float), ("causal", ctypes.c_int), ("stream", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load(path: str | None = None):
+    """Load the HIP library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise FaError(-1, f"{path} is missing: build it with `python -m exact_attention_116_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, F, I]
+    lib.fa_fwd.restype = I
+    lib.fa_fwd_ex.argtypes = [ctypes.POINTER(fa_fwd_params)]
+    lib.fa_fwd_ex.restype = I
+    lib.fa_decode_splitkv.argtypes = [P, P, P, P, I, I, I, I, I]
+    lib.fa_decode_splitkv.restype = I
+    lib.fa_decode_workspace_bytes.argtypes = [I, I, I, I]
+    lib.fa_decode_workspace_bytes.restype = Z
+    lib.fa_decode_splitkv_ex.argtypes = [P, P, P, P, P, I, I, I, I, I, F, P, Z, P]
+    lib.fa_decode_splitkv_ex.restype = I
+    lib.fa_status_string.argtypes = [I]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_last_error.argtypes = []
+    lib.fa_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _ptr(x):
+    """Device address of a tensor (``data_ptr()``), an int, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        return None
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(status: int, what: str):
+    if status != FA_OK:
+        lib = load()
+        raise FaError(status, f"{what}: {lib.fa_status_string(status).decode()}: "
+                              f"{lib.fa_last_error().decode()}")
+
+
+def fa_status_string(status: int) -> str:
+    return load().fa_status_string(status).decode()
+
+
+def fa_last_error() -> str:
+    return load().fa_last_error().decode()
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal):
+    """bf16 [B,H,N,d] q, k, v -> bf16 o, fp32 lse [B,H,N]; default stream."""
+    _check(load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                         float(scale), int(bool(causal))), "fa_fwd")
+
+
+def fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, in_dtype=FA_BF16, out_dtype=FA_BF16,
+              q_scale=None, k_scale=None, v_scale=None, stream=None):
+    p = fa_fwd_params(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(q_scale),
+                      _ptr(k_scale), _ptr(v_scale), in_dtype, out_dtype, B, H, N, d,
+                      float(scale), int(bool(causal)), _stream(stream))
+    _check(load().fa_fwd_ex(ctypes.byref(p)), "fa_fwd_ex")
+
+
+def fa_decode_splitkv(q, kcache, vcache, o, B, H, Lkv, d, num_splits):
+    _check(load().fa_decode_splitkv(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(o), B, H, Lkv, d,
+                                    num_splits), "fa_decode_splitkv")
+
+
+def fa_decode_workspace_bytes(B, H, d, num_splits) -> int:
+    return int(load().fa_decode_workspace_bytes(B, H, d, num_splits))
+
+
+def fa_decode_splitkv_ex(q, kcache, vcache, o, lse, B, H, Lkv, d, num_splits, scale, workspace,
+                         workspace_bytes, stream=None):
+    _check(load().fa_decode_splitkv_ex(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(o), _ptr(lse),
+                                       B, H, Lkv, d, num_splits, float(scale), _ptr(workspace),
+                                       int(workspace_bytes), _stream(stream)),
+           "fa_decode_splitkv_ex")

@@ -1,0 +1,217 @@
+// C-ABI host layer of the attention library: argument validation, the
+// library-owned decode workspace and dispatch to the HIP launchers.
+// Every check runs before any HIP call, so a rejected call touches no device.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fa_status fail(fa_status s, const char* what) {
+  g_last_error = what;
+  return s;
+}
+
+fa_status hip_fail(hipError_t e, const char* where) {
+  g_last_error = std::string(where) + ": " + hipGetErrorString(e);
+  return FA_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool good_scale(float s) { return std::isfinite(s) && s > 0.f; }
+
+constexpr double kLog2e = 1.4426950408889634074;
+
+fa_status check_fwd(const fa_fwd_params* p) {
+  if (!p) return fail(FA_ERR_INVALID_ARG, "params is NULL");
+  if (!aligned16(p->q) || !aligned16(p->k) || !aligned16(p->v) || !aligned16(p->o) ||
+      !aligned16(p->lse))
+    return fail(FA_ERR_INVALID_ARG, "q, k, v, o and lse must be non-NULL and 16-byte aligned");
+  if (p->B < 1 || p->H < 1 || p->N < 1)
+    return fail(FA_ERR_INVALID_ARG, "B, H and N must be >= 1");
+  if (p->d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1");
+  if (!good_scale(p->scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (p->out_dtype != FA_BF16 && p->out_dtype != FA_FP32)
+    return fail(FA_ERR_INVALID_ARG, "out_dtype must be FA_BF16 or FA_FP32");
+  const long long elems = (long long)p->B * p->H * p->N * p->d;
+  if ((long long)p->B * p->H * ((p->N + 31) / 32) > 0x7FFFFFFFLL || elems <= 0)
+    return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
+  if (p->in_dtype == FA_BF16) {
+    if (p->q_scale || p->k_scale || p->v_scale)
+      return fail(FA_ERR_INVALID_ARG, "block scales are only accepted with FA_FP8_E4M3 inputs");
+    if (p->d != 64 && p->d != 128) return fail(FA_ERR_UNSUPPORTED, "bf16 path supports d = 64 or 128");
+    return FA_OK;
+  }
+  if (p->in_dtype == FA_FP8_E4M3) {
+    if (!p->q_scale || !p->k_scale || !p->v_scale)
+      return fail(FA_ERR_INVALID_ARG, "fp8 inputs need q_scale, k_scale and v_scale");
+    if ((reinterpret_cast<uintptr_t>(p->q_scale) | reinterpret_cast<uintptr_t>(p->k_scale) |
+         reinterpret_cast<uintptr_t>(p->v_scale)) & 3u)
+      return fail(FA_ERR_INVALID_ARG, "block scales must be 4-byte aligned");
+    if (p->d != 128) return fail(FA_ERR_UNSUPPORTED, "fp8 path supports d = 128");
+    return FA_OK;
+  }
+  return fail(FA_ERR_INVALID_ARG, "in_dtype must be FA_BF16 or FA_FP8_E4M3");
+}
+
+fa_status run_fwd(const fa_fwd_params* p) {
+  fa_status st = check_fwd(p);
+  if (st != FA_OK) return st;
+  fa::FwdArgs a{};
+  a.q = p->q; a.k = p->k; a.v = p->v; a.o = p->o; a.lse = p->lse;
+  a.q_scale = p->q_scale; a.k_scale = p->k_scale; a.v_scale = p->v_scale;
+  a.B = p->B; a.H = p->H; a.N = p->N; a.d = p->d;
+  a.scale = p->scale;
+  a.scale_log2 = (float)((double)p->scale * kLog2e);
+  a.causal = p->causal != 0;
+  a.out_f32 = p->out_dtype == FA_FP32;
+  a.stream = p->stream;
+  hipError_t e = (p->in_dtype == FA_FP8_E4M3) ? fa::launch_fwd_fp8(a) : fa::launch_fwd_bf16(a);
+  if (e == hipErrorNotSupported) return fail(FA_ERR_UNSUPPORTED, "fp8 forward is not built");
+  if (e != hipSuccess) return hip_fail(e, "fa_fwd launch");
+  g_last_error.clear();
+  return FA_OK;
+}
+
+size_t decode_ws_bytes(int B, int H, int d, int S) {
+  const size_t n = (size_t)B * H * S * (size_t)(d + 1) * 4u;
+  return (n + 255u) & ~(size_t)255u;
+}
+
+fa_status check_decode(const void* q, const void* kc, const void* vc, const void* o, int B, int H,
+                       int Lkv, int d, int S, float scale) {
+  if (!aligned16(q) || !aligned16(kc) || !aligned16(vc) || !aligned16(o))
+    return fail(FA_ERR_INVALID_ARG, "q, kcache, vcache and o must be non-NULL and 16-byte aligned");
+  if (B < 1 || H < 1 || Lkv < 1) return fail(FA_ERR_INVALID_ARG, "B, H and Lkv must be >= 1");
+  if (S < 1 || S > Lkv) return fail(FA_ERR_INVALID_ARG, "num_splits must be in [1, Lkv]");
+  if (d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1");
+  if (!good_scale(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "decode supports d = 64 or 128");
+  if ((long long)B * H * S > 0x7FFFFFFFLL) return fail(FA_ERR_INVALID_ARG, "B*H*num_splits too large");
+  return FA_OK;
+}
+
+fa_status run_decode(const void* q, const void* kc, const void* vc, void* o, float* lse, int B,
+                     int H, int Lkv, int d, int S, float scale, void* ws, void* stream) {
+  fa::DecodeArgs a{};
+  a.q = q; a.k = kc; a.v = vc; a.o = o; a.lse = lse;
+  a.part_o = static_cast<float*>(ws);
+  a.part_lse = static_cast<float*>(ws) + (size_t)B * H * S * d;
+  a.B = B; a.H = H; a.Lkv = Lkv; a.d = d; a.num_splits = S;
+  a.scale_log2 = (float)((double)scale * kLog2e);
+  a.stream = stream;
+  hipError_t e = fa::launch_decode(a);
+  if (e != hipSuccess) return hip_fail(e, "fa_decode_splitkv launch");
+  g_last_error.clear();
+  return FA_OK;
+}
+
+// Library-owned decode workspace: one buffer per device, grown on demand and
+// kept until the process ends.
+struct OwnedWorkspace {
+  std::mutex mu;
+  std::vector<void*> ptr;
+  std::vector<size_t> bytes;
+};
+OwnedWorkspace g_ws;
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int N, int d, float scale, int causal) {
+  fa_fwd_params p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.in_dtype = FA_BF16;
+  p.out_dtype = FA_BF16;
+  p.B = B; p.H = H; p.N = N; p.d = d;
+  p.scale = scale;
+  p.causal = causal;
+  p.stream = nullptr;
+  return run_fwd(&p);
+}
+
+fa_status fa_fwd_ex(const fa_fwd_params* p) { return run_fwd(p); }
+
+size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits) {
+  if (B < 1 || H < 1 || num_splits < 1 || (d != 64 && d != 128)) return 0;
+  return decode_ws_bytes(B, H, d, num_splits);
+}
+
+fa_status fa_decode_splitkv_ex(const void* q, const void* kcache, const void* vcache, void* o,
+                               float* lse, int B, int H, int Lkv, int d, int num_splits,
+                               float scale, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  fa_status st = check_decode(q, kcache, vcache, o, B, H, Lkv, d, num_splits, scale);
+  if (st != FA_OK) return st;
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (!aligned16(workspace)) return fail(FA_ERR_WORKSPACE, "workspace must be non-NULL and 16-byte aligned");
+  if (workspace_bytes < decode_ws_bytes(B, H, d, num_splits))
+    return fail(FA_ERR_WORKSPACE, "workspace smaller than fa_decode_workspace_bytes()");
+  return run_decode(q, kcache, vcache, o, lse, B, H, Lkv, d, num_splits, scale, workspace, stream);
+}
+
+fa_status fa_decode_splitkv(const void* q, const void* kcache, const void* vcache, void* o, int B,
+                            int H, int Lkv, int d, int num_splits) {
+  const float scale = d > 0 ? (float)(1.0 / std::sqrt((double)d)) : 0.f;
+  fa_status st = check_decode(q, kcache, vcache, o, B, H, Lkv, d, num_splits, scale);
+  if (st != FA_OK) return st;
+  const size_t need = decode_ws_bytes(B, H, d, num_splits);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_ws.mu);
+    if ((int)g_ws.ptr.size() <= dev) {
+      g_ws.ptr.resize(dev + 1, nullptr);
+      g_ws.bytes.resize(dev + 1, 0);
+    }
+    if (g_ws.bytes[dev] < need) {
+      if (g_ws.ptr[dev]) {
+        // the old buffer may still be read by queued work of an earlier call
+        e = hipDeviceSynchronize();
+        if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+        hipFree(g_ws.ptr[dev]);
+        g_ws.ptr[dev] = nullptr;
+        g_ws.bytes[dev] = 0;
+      }
+      e = hipMalloc(&g_ws.ptr[dev], need);
+      if (e != hipSuccess) {
+        g_ws.ptr[dev] = nullptr;
+        return fail(FA_ERR_WORKSPACE, "could not allocate the decode workspace");
+      }
+      g_ws.bytes[dev] = need;
+    }
+    ws = g_ws.ptr[dev];
+  }
+  return run_decode(q, kcache, vcache, o, nullptr, B, H, Lkv, d, num_splits, scale, ws, nullptr);
+}
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+  }
+  return "FA_UNKNOWN_STATUS";
+}
+
+const char* fa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

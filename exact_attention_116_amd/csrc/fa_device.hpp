@@ -1,0 +1,87 @@
+// Device-side helpers shared by the gfx950 attention kernels: vector types,
+// MFMA wrappers, wave64 cross-lane reductions and bf16 packing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ float as_f32(uint32_t x) { return __builtin_bit_cast(float, x); }
+__device__ __forceinline__ uint32_t as_u32(float x) { return __builtin_bit_cast(uint32_t, x); }
+
+// D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16) on the matrix cores.
+// Operand layout (wave64): lane l supplies row (A) / column (B) l%32 and
+// eight consecutive contraction slots 8*(l/32)..+7.  Result layout: lane l
+// holds column l%32, rows 8*(i/4) + 4*(l/32) + i%4 for i = 0..15.
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Both halves of the wave exchange a value: returns {x[l%32], x[32 + l%32]}
+// in some order, so op(r.x, r.y) is the pairwise reduction over l and l^32.
+__device__ __forceinline__ float max_pair32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(x), false, false);
+  return fmaxf(as_f32(r[0]), as_f32(r[1]));
+}
+__device__ __forceinline__ float sum_pair32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(x), false, false);
+  return as_f32(r[0]) + as_f32(r[1]);
+}
+
+// DPP lane permutations within 16-lane rows.
+enum : int {
+  kDppQuadXor1 = 0xB1,        // quad_perm [1,0,3,2]
+  kDppQuadXor2 = 0x4E,        // quad_perm [2,3,0,1]
+  kDppRowMirror = 0x140,      // lane i <- lane 15-i (within 16)
+  kDppRowHalfMirror = 0x141,  // lane i <- lane 7-i (within 8)
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return as_f32(__builtin_amdgcn_mov_dpp(as_u32(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of G lanes (G = 8 or 16); every lane gets the total.
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(G == 8 || G == 16, "group of 8 or 16 lanes");
+  if constexpr (G == 16) x += dpp<kDppRowMirror>(x);
+  x += dpp<kDppRowHalfMirror>(x);
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppQuadXor1>(x);
+  return x;
+}
+
+// v_dot2_f32_bf16: acc + a.lo*b.lo + a.hi*b.hi for bf16 pairs packed in dwords.
+// (The operands are plain dwords: a bit_cast applied to a vector element
+// expression directly has been seen to read element 0 only.)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
+                                         acc, false);
+}
+
+// bf16 pair (packed in a dword) -> two floats.
+__device__ __forceinline__ float bf16lo(uint32_t w) { return as_f32(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return as_f32(w & 0xFFFF0000u); }
+
+// Round two floats to bf16 (nearest even) and pack them (a in the low half).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  bf16x2 p = {(bf16)a, (bf16)b};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+}  // namespace fa

@@ -1,0 +1,44 @@
+// Launcher interface between the C-ABI host layer (fa_api.cpp) and the HIP
+// kernels.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const float* q_scale;  // fp8 only
+  const float* k_scale;
+  const float* v_scale;
+  int B, H, N, d;
+  float scale;        // softmax scale
+  float scale_log2;   // scale * log2(e)
+  int causal;
+  int out_f32;
+  void* stream;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;         // may be null
+  float* part_o;      // [B*H, S, d] fp32
+  float* part_lse;    // [B*H, S]    fp32
+  int B, H, Lkv, d, num_splits;
+  float scale_log2;
+  void* stream;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_fwd_fp8(const FwdArgs& a);
+hipError_t launch_decode(const DecodeArgs& a);
+
+}  // namespace fa

@@ -1,0 +1,148 @@
+/*
+ * fa.h -- exact attention (FlashAttention forward, split-KV decode) on
+ * AMD Instinct MI355X (gfx950).  C ABI: plain pointers and sizes only.
+ *
+ * What is computed (per batch b, head h; row-major [B, H, N, d] tensors,
+ * the (batch, heads, seq_len, head_dim) layout of the "Flash Attention"
+ * Markdown note, section "问题分析" / problem analysis):
+ *
+ *     s_ij  = scale * <q_i, k_j>          (j > i masked when causal)
+ *     O_i   = sum_j softmax_j(s_ij) * v_j
+ *     LSE_i = ln sum_j exp(s_ij)          (natural log, fp32)
+ *
+ * The N x N score matrix is never written to memory: queries are tiled in
+ * the outer loop and keys/values in the inner loop with a running row max
+ * and running sum (same note, "Tiling（分块）技术" and "递归计算softmax";
+ * the FlashAttention-2 overview's Q-outer / KV-inner loop order).
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library never frees or retains them.  They must be non-NULL and
+ *     16-byte aligned; tensors are dense (contiguous) in the stated layout.
+ *   - Calls are asynchronous on the given stream (NULL = the default
+ *     stream); results are valid after the caller synchronises.
+ *   - Argument errors are reported by the return value before anything is
+ *     launched; nothing crosses the ABI as an exception.  A launch failure
+ *     returns FA_ERR_HIP (fa_last_error() has the HIP text); faults inside a
+ *     kernel surface at the caller's next synchronisation.
+ *   - Calls that share a library-owned workspace (fa_decode_splitkv) on one
+ *     device must not run concurrently on different streams.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size, bad scale */
+  FA_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement (e.g. d=96) */
+  FA_ERR_WORKSPACE = 3,     /* workspace too small or could not be allocated */
+  FA_ERR_HIP = 4            /* the HIP runtime reported an error */
+} fa_status;
+
+typedef enum {
+  FA_BF16 = 0,
+  FA_FP32 = 1,
+  FA_FP8_E4M3 = 2           /* OCP E4M3FN (bias 7, max 448), block-scaled */
+} fa_dtype;
+
+/*
+ * fa_fwd -- attention forward pass, bf16 in, bf16 out, fp32 LSE.
+ *
+ * q, k, v : bf16 [B, H, N, d]      o : bf16 [B, H, N, d]
+ * lse     : fp32 [B, H, N]         (natural-log log-sum-exp of the scaled scores)
+ * d in {64, 128}; N >= 1 (any length; tails are masked); B, H >= 1;
+ * scale finite and > 0 (the usual value is 1/sqrt(d), the softmax_scale
+ * default of the flash_attn_func call in the note's "框架集成" section);
+ * causal != 0 masks key j > query i (the causal=True option of the note's
+ * "使用注意事项" usage notes).  Runs on the default stream.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, float scale, int causal);
+
+/*
+ * fa_fwd_ex -- the forward pass with dtype and stream options.
+ *
+ * in_dtype  FA_BF16     : q, k, v bf16 [B,H,N,d]; q_scale/k_scale/v_scale must be NULL.
+ * in_dtype  FA_FP8_E4M3 : q, k, v E4M3FN codes [B,H,N,d] (1 byte each) with
+ *                         one fp32 scale per 64 consecutive rows of each
+ *                         (b, h): q_scale, k_scale, v_scale fp32
+ *                         [B, H, ceil(N/64)]; element value = code * scale
+ *                         (the block quantisation of the FlashAttention-3
+ *                         snippets).  The kernel rounds the probabilities
+ *                         to E4M3FN for the P*V product; d must be 128.
+ * out_dtype FA_BF16 or FA_FP32 : o is [B,H,N,d] of that type.
+ * lse fp32 [B,H,N] (required).  stream is a hipStream_t (NULL = default).
+ */
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const float* q_scale;
+  const float* k_scale;
+  const float* v_scale;
+  int in_dtype;   /* fa_dtype */
+  int out_dtype;  /* fa_dtype */
+  int B, H, N, d;
+  float scale;
+  int causal;
+  void* stream;
+} fa_fwd_params;
+
+fa_status fa_fwd_ex(const fa_fwd_params* p);
+
+/*
+ * fa_decode_splitkv -- single-query decode with the KV length split across
+ * workgroups (the Flash-Decoding scheme of the FlashAttention-2 overview
+ * snippets: K and V cut into parts, each part gives a partial output, the
+ * partial outputs are merged; the FlashAttention-3 snippets call the merge
+ * the splitK combine).
+ *
+ * q      : bf16 [B, H, 1, d]          o : bf16 [B, H, 1, d]
+ * kcache, vcache : bf16 [B, H, Lkv, d]   (no mask; every key is visible)
+ * num_splits in [1, Lkv]: split s covers keys [s*c, min((s+1)*c, Lkv)),
+ * c = ceil(Lkv / num_splits).  scale = 1/sqrt(d).  d in {64, 128}.
+ * Each split writes a normalised partial O_s and its LSE_s (fp32) to a
+ * workspace; a second kernel merges them with weights exp(LSE_s - LSE).
+ * The workspace is owned by the library, grown on demand per device and
+ * kept until the process ends (it allocates; see fa_decode_splitkv_ex for
+ * a caller-provided workspace).  Default stream.
+ */
+fa_status fa_decode_splitkv(const void* q, const void* kcache, const void* vcache, void* o,
+                            int B, int H, int Lkv, int d, int num_splits);
+
+/* Bytes of workspace fa_decode_splitkv_ex needs: B*H*num_splits*(d+1)*4,
+ * rounded up to 256.  Returns 0 for arguments fa_decode_splitkv would reject. */
+size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits);
+
+/*
+ * fa_decode_splitkv_ex -- as fa_decode_splitkv, plus: an explicit softmax
+ * scale (finite, > 0); lse fp32 [B, H] (may be NULL); a caller-owned device
+ * workspace of at least fa_decode_workspace_bytes() bytes (16-byte aligned;
+ * FA_ERR_WORKSPACE if smaller); and a stream.  Layout of the workspace after
+ * the call: partial O fp32 [B, H, num_splits, d], then partial LSE fp32
+ * [B, H, num_splits] (an empty split has O = 0, LSE = -inf).
+ */
+fa_status fa_decode_splitkv_ex(const void* q, const void* kcache, const void* vcache, void* o,
+                               float* lse, int B, int H, int Lkv, int d, int num_splits,
+                               float scale, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* A static string naming the status. */
+const char* fa_status_string(fa_status s);
+
+/* The message of the last failing call on this thread ("" if none). */
+const char* fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,122 @@
+"""The C-ABI library without a GPU: it loads, exports what include/fa.h
+declares, and rejects bad arguments before touching any device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_116_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+A = 0x10000          # a 16-byte-aligned fake device address (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fa.load()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(fa.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert fa.fa_status_string(fa.FA_OK) == "FA_OK"
+    assert fa.fa_status_string(fa.FA_ERR_WORKSPACE) == "FA_ERR_WORKSPACE"
+    assert fa.fa_status_string(99) == "FA_UNKNOWN_STATUS"
+
+
+def test_params_struct_matches_header():
+    # pointer fields, then 2 dtype ints, 4 sizes, float scale, int causal, stream
+    assert ctypes.sizeof(fa.fa_fwd_params) == 8 * 8 + 4 * 8 + 8
+
+
+def _fwd(lib, q=A, k=A, v=A, o=A, lse=A, B=1, H=1, N=16, d=128, scale=0.1, causal=0):
+    return lib.fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=None), fa.FA_ERR_INVALID_ARG),
+    (dict(k=A + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(H=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+])
+def test_fwd_rejects(lib, kw, status):
+    assert _fwd(lib, **kw) == status
+    assert fa.fa_last_error() != ""
+
+
+def test_fwd_ex_rejects(lib):
+    assert lib.fa_fwd_ex(None) == fa.FA_ERR_INVALID_ARG
+    p = fa.fa_fwd_params(A, A, A, A, A, None, None, None, fa.FA_FP8_E4M3, fa.FA_BF16,
+                         1, 1, 64, 128, 0.1, 1, None)
+    assert lib.fa_fwd_ex(ctypes.byref(p)) == fa.FA_ERR_INVALID_ARG      # missing scales
+    p.q_scale = p.k_scale = p.v_scale = A
+    p.d = 64
+    assert lib.fa_fwd_ex(ctypes.byref(p)) == fa.FA_ERR_UNSUPPORTED      # fp8 needs d=128
+    p.in_dtype = fa.FA_BF16
+    p.d = 128
+    assert lib.fa_fwd_ex(ctypes.byref(p)) == fa.FA_ERR_INVALID_ARG      # scales with bf16
+    p.q_scale = p.k_scale = p.v_scale = None
+    p.out_dtype = fa.FA_FP8_E4M3
+    assert lib.fa_fwd_ex(ctypes.byref(p)) == fa.FA_ERR_INVALID_ARG      # fp8 output
+    p.out_dtype = fa.FA_FP32
+    p.in_dtype = 7
+    assert lib.fa_fwd_ex(ctypes.byref(p)) == fa.FA_ERR_INVALID_ARG
+
+
+def test_workspace_bytes(lib):
+    assert fa.fa_decode_workspace_bytes(8, 32, 128, 64) == 8 * 32 * 64 * 129 * 4
+    assert fa.fa_decode_workspace_bytes(1, 1, 64, 3) == 1024          # 780 rounded up to 256
+    assert fa.fa_decode_workspace_bytes(1, 1, 96, 3) == 0
+    assert fa.fa_decode_workspace_bytes(0, 1, 128, 3) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(kc=A + 4), fa.FA_ERR_INVALID_ARG),
+    (dict(S=0), fa.FA_ERR_INVALID_ARG),
+    (dict(S=17), fa.FA_ERR_INVALID_ARG),     # more splits than keys
+    (dict(Lkv=0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=100), fa.FA_ERR_WORKSPACE),
+])
+def test_decode_ex_rejects(lib, kw, status):
+    a = dict(q=A, kc=A, vc=A, o=A, lse=None, B=1, H=2, Lkv=16, d=128, S=4, scale=0.1,
+             ws=A, ws_bytes=1 << 20)
+    a.update(kw)
+    st = lib.fa_decode_splitkv_ex(a["q"], a["kc"], a["vc"], a["o"], a["lse"], a["B"], a["H"],
+                                  a["Lkv"], a["d"], a["S"], a["scale"], a["ws"], a["ws_bytes"], None)
+    assert st == status
+
+
+def test_decode_rejects(lib):
+    assert lib.fa_decode_splitkv(A, A, A, None, 1, 1, 16, 128, 4) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_decode_splitkv(A, A, A, A, 1, 1, 16, 128, 32) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_decode_splitkv(A, A, A, A, 1, 1, 16, 32, 4) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_binding_raises_with_status():
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_fwd(A, A, A, A, None, 1, 1, 16, 128, 0.1, False)
+    assert e.value.status == fa.FA_ERR_INVALID_ARG and "lse" in str(e.value)

@@ -1,0 +1,94 @@
+"""GPU parity of the split-KV decode (partials and merge) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import fa_inputs as fi
+import oracle
+from _gpu_util import bf16_to_dev, check_bf16_gates, dev_to_f64, say
+
+pytestmark = pytest.mark.gpu
+
+
+def gen(wid, B, H, Lkv, d):
+    q = fi.bf16_tensor(wid, fi.Q_ID, B, H, 1, d)
+    k = fi.bf16_tensor(wid, fi.K_ID, B, H, Lkv, d)
+    v = fi.bf16_tensor(wid, fi.V_ID, B, H, Lkv, d)
+    return q, k, v
+
+
+def run_ex(fa, q, k, v, B, H, Lkv, d, S, scale):
+    o = torch.empty((B, H, 1, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    nbytes = fa.fa_decode_workspace_bytes(B, H, d, S)
+    ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    fa.fa_decode_splitkv_ex(q, k, v, o, lse, B, H, Lkv, d, S, scale, ws, nbytes)
+    torch.cuda.synchronize()
+    po = ws[:B * H * S * d].view(B, H, S, d)
+    pl = ws[B * H * S * d:B * H * S * (d + 1)].view(B, H, S)
+    return o, lse, po, pl
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Lkv,S", [(1, 1), (5, 4), (70, 64), (100, 3), (1000, 64), (4097, 7),
+                                   (4096, 1), (333, 333), (20000, 64)])
+def test_decode_small(gpu_lib, Lkv, S, d):
+    fa = gpu_lib
+    B, H = 2, 3
+    wid = 4000 + Lkv + S + d
+    say(f"decode B={B} H={H} Lkv={Lkv} d={d} splits={S} seed-id={wid}")
+    qb, kb, vb = gen(wid, B, H, Lkv, d)
+    scale = d ** -0.5
+    o, lse, po, pl = run_ex(fa, *map(bf16_to_dev, (qb, kb, vb)), B, H, Lkv, d, S, scale)
+    q, k, v = map(oracle.decode_bf16, (qb, kb, vb))
+    O, L = oracle.decode_attention(q, k, v, scale)
+    check_bf16_gates(dev_to_f64(o)[:, :, 0], O[:, :, 0], dev_to_f64(lse), L[:, :, 0], "merged")
+    Os, Ls = oracle.split_partials(q, k, v, scale, S)
+    pog, plg = dev_to_f64(po), dev_to_f64(pl)
+    empty = np.isneginf(Ls[:, :, :, 0])
+    assert np.array_equal(np.isneginf(plg), empty)
+    assert np.all(pog[empty] == 0)
+    err = np.abs(pog - Os[:, :, :, 0])
+    assert err.max() <= 2e-3, err.max()     # fp32 partials: bf16 inputs, fp32 math
+    lr = np.abs(plg[~empty] - Ls[:, :, :, 0][~empty]) / np.maximum(np.abs(Ls[:, :, :, 0][~empty]), 1)
+    assert lr.max() <= 1e-5, lr.max()
+
+
+def test_decode_default_entry_point(gpu_lib):
+    fa = gpu_lib
+    B, H, Lkv, d, S = 2, 4, 3000, 128, 16
+    say("decode via fa_decode_splitkv (library-owned workspace)")
+    qb, kb, vb = gen(4500, B, H, Lkv, d)
+    q, k, v = map(bf16_to_dev, (qb, kb, vb))
+    o = torch.empty((B, H, 1, d), dtype=torch.bfloat16, device="cuda")
+    fa.fa_decode_splitkv(q, k, v, o, B, H, Lkv, d, S)
+    torch.cuda.synchronize()
+    O, L = oracle.decode_attention(*map(oracle.decode_bf16, (qb, kb, vb)), d ** -0.5)
+    err = np.abs(dev_to_f64(o) - O)
+    assert err.max() <= 1e-2 and err.mean() <= 1e-3
+    # a second, larger call grows the workspace
+    o2 = torch.empty_like(o)
+    fa.fa_decode_splitkv(q, k, v, o2, B, H, Lkv, d, 3000)
+    torch.cuda.synchronize()
+    assert np.abs(dev_to_f64(o2) - O).max() <= 1e-2
+
+
+def test_decode_full_size(gpu_lib):
+    """B=8, H=32, Lkv=65536, d=128, 64 splits; sampled (b,h) against the oracle,
+    every (b,h) against the single-split run of the same kernel pair."""
+    fa = gpu_lib
+    w = fi.WORKLOADS[4]
+    say(f"decode {w.name}: generating 8 GiB of K/V")
+    qb, kb, vb = gen(w.wid, w.B, w.H, w.Lkv, w.d)
+    q, k, v = map(bf16_to_dev, (qb, kb, vb))
+    say("decode full size: running")
+    o, lse, _, _ = run_ex(fa, q, k, v, w.B, w.H, w.Lkv, w.d, w.num_splits, w.scale)
+    og, lg = dev_to_f64(o), dev_to_f64(lse)
+    assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg))
+    for b, h in [(0, 0), (3, 17), (7, 31)]:
+        Q, K, V = (oracle.decode_bf16(x[b, h]) for x in (qb, kb, vb))
+        O, L = oracle.decode_attention(Q, K, V, w.scale)
+        check_bf16_gates(og[b, h], O, lg[b, h:h + 1], L, f"(b={b},h={h})")
+    o1, lse1, _, _ = run_ex(fa, q, k, v, w.B, w.H, w.Lkv, w.d, 1, w.scale)
+    assert np.abs(dev_to_f64(o1) - og).max() <= 1e-2
+    assert np.abs(dev_to_f64(lse1) - lg).max() <= 1e-3
