@@ -44,6 +44,11 @@ def decode_bytes(w):
     return kv + 2 * w.B * w.H * w.d * 2
 
 
+def log(msg):
+    """Progress on stderr; the JSON result is the only line on stdout."""
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
 def cpu_info():
     model = platform.processor() or ""
     try:
@@ -140,6 +145,7 @@ def main():
 
     w2, w3, w4, w5 = (fi.WORKLOADS[i] for i in (2, 3, 4, 5))
     if want("c2c") or want("c2n"):
+        log("generating B=2 H=32 N=2048 d=128 inputs")
         q2, k2, v2 = (up_bf16(fi.bf16_tensor(w2.wid, t, w2.B, w2.H, w2.N, w2.d)) for t in range(3))
         o2 = torch.empty_like(q2)
         l2 = torch.empty((w2.B, w2.H, w2.N), dtype=torch.float32, device=dev)
@@ -149,6 +155,7 @@ def main():
                     q2, k2, v2, o2, l2, w2.B, w2.H, w2.N, w2.d, w2.scale, c, stream=stream)),
                     fwd_flops(w2, causal), fwd_bytes(w2), "fwd_bf16"))
     if want("c3"):
+        log("generating B=1 H=16 N=16384 d=128 inputs")
         q3, k3, v3 = (up_bf16(fi.bf16_tensor(w3.wid, t, w3.B, w3.H, w3.N, w3.d)) for t in range(3))
         o3 = torch.empty_like(q3)
         l3 = torch.empty((w3.B, w3.H, w3.N), dtype=torch.float32, device=dev)
@@ -156,6 +163,7 @@ def main():
                                                 w3.scale, True, stream=stream),
                      fwd_flops(w3, True), fwd_bytes(w3), "fwd_bf16"))
     if want("c4"):
+        log("generating decode B=8 H=32 Lkv=65536 d=128 inputs (8 GiB)")
         q4 = up_bf16(fi.bf16_tensor(w4.wid, 0, w4.B, w4.H, 1, w4.d))
         k4 = up_bf16(fi.bf16_tensor(w4.wid, 1, w4.B, w4.H, w4.Lkv, w4.d))
         v4 = up_bf16(fi.bf16_tensor(w4.wid, 2, w4.B, w4.H, w4.Lkv, w4.d))
@@ -212,6 +220,7 @@ def main():
             if evs is not None:
                 evs[i][1].record(stream)
 
+    log(f"warmup {args.warmup} steps over {[j[0] for j in jobs]}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -282,7 +291,9 @@ def main():
                    "gcn_arch": getattr(prop, "gcnArchName", "")},
         "wall_s_timed": wall,
     }
+    log(f"timed {args.steps} steps in {wall:.2f} s")
     if not args.no_cpu_baseline and args.only == "all":
+        log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

@@ -60,6 +60,7 @@ fa_status check_fwd(const fa_fwd_params* p) {
          reinterpret_cast<uintptr_t>(p->v_scale)) & 3u)
       return fail(FA_ERR_INVALID_ARG, "block scales must be 4-byte aligned");
     if (p->d != 128) return fail(FA_ERR_UNSUPPORTED, "fp8 path supports d = 128");
+    if (p->out_dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "fp8 path writes bf16 output");
     return FA_OK;
   }
   return fail(FA_ERR_INVALID_ARG, "in_dtype must be FA_BF16 or FA_FP8_E4M3");
@@ -78,7 +79,7 @@ fa_status run_fwd(const fa_fwd_params* p) {
   a.out_f32 = p->out_dtype == FA_FP32;
   a.stream = p->stream;
   hipError_t e = (p->in_dtype == FA_FP8_E4M3) ? fa::launch_fwd_fp8(a) : fa::launch_fwd_bf16(a);
-  if (e == hipErrorNotSupported) return fail(FA_ERR_UNSUPPORTED, "fp8 forward is not built");
+  if (e == hipErrorNotSupported) return fail(FA_ERR_UNSUPPORTED, "no kernel for this request");
   if (e != hipSuccess) return hip_fail(e, "fa_fwd launch");
   g_last_error.clear();
   return FA_OK;

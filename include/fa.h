@@ -72,11 +72,17 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  * in_dtype  FA_FP8_E4M3 : q, k, v E4M3FN codes [B,H,N,d] (1 byte each) with
  *                         one fp32 scale per 64 consecutive rows of each
  *                         (b, h): q_scale, k_scale, v_scale fp32
- *                         [B, H, ceil(N/64)]; element value = code * scale
- *                         (the block quantisation of the FlashAttention-3
- *                         snippets).  The kernel rounds the probabilities
- *                         to E4M3FN for the P*V product; d must be 128.
- * out_dtype FA_BF16 or FA_FP32 : o is [B,H,N,d] of that type.
+ *                         [B, H, ceil(N/64)], finite and > 0; element
+ *                         value = code * scale (the block quantisation of
+ *                         the FlashAttention-3 snippets).  Both products run
+ *                         on fp8 matrix cores with fp32 accumulation: the
+ *                         unnormalised probabilities of keys in V block t
+ *                         (at most 2^0.75 each) are multiplied by
+ *                         256 * v_scale[t] / max(v_scale of the head) and
+ *                         rounded to E4M3FN for the P*V product; the row sum
+ *                         uses the unrounded fp32 values.  d must be 128 and
+ *                         out_dtype FA_BF16 (else FA_ERR_UNSUPPORTED).
+ * out_dtype FA_BF16 or FA_FP32 (bf16 inputs) : o is [B,H,N,d] of that type.
  * lse fp32 [B,H,N] (required).  stream is a hipStream_t (NULL = default).
  */
 typedef struct {

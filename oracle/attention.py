@@ -31,6 +31,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from .codecs import round_to_e4m3fn
+
 ROW_BLOCK = 512
 
 
@@ -206,3 +208,39 @@ def fp8_p_error_bound(q, k, v, scale, causal, p_prescale, qidx=None):
     Bnd = (16.0 / 15.0) * (2.0 ** -4 * rel_term + 2.0 ** -10 / p_prescale * abs_term) \
         + 2.0 ** -8 * absO + 1e-4
     return O, lse, Bnd
+
+
+def fp8_p_attention(q, k, v, scale, causal, p_scale, qidx=None):
+    """Attention whose probability weights are rounded to E4M3FN before the
+    P*V product -- the precision of the fp8 path of the FlashAttention-3
+    snippets, where the second product also runs in fp8 -- with everything
+    else exact.
+
+    It states the error that rounding P alone causes, as a yardstick for the
+    typical (mean) error of an fp8 kernel; the exact result is ``attention``.
+    For each query row: p_ij = exp(s_ij - m_i) with the row's true max;
+    key j's weight is rounded as round_e4m3(p_ij * p_scale[j]) / p_scale[j];
+    O_i = sum_j rounded_ij v_j / sum_j p_ij (the unrounded row sum).
+
+    q [r, d] (rows ``qidx``), k, v [Nk, d] of one (batch, head), float64;
+    p_scale [Nk] > 0.  Returns O [r, d].
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    sig = np.asarray(p_scale, np.float64)
+    if qidx is None:
+        qidx = np.arange(q.shape[0])
+    qidx = np.asarray(qidx, np.int64)
+    O = np.empty((q.shape[0], v.shape[1]))
+    for r0 in range(0, q.shape[0], ROW_BLOCK):
+        sl = slice(r0, r0 + ROW_BLOCK)
+        S = scale * (q[sl] @ k.T)
+        if causal:
+            j = np.arange(k.shape[0])
+            S = np.where(j[None, :] <= qidx[sl, None], S, -np.inf)
+        m = S.max(axis=1)
+        P = np.exp(S - m[:, None])
+        Ph = round_to_e4m3fn(P * sig[None, :]) / sig[None, :]
+        O[sl] = (Ph @ v) / P.sum(axis=1)[:, None]
+    return O

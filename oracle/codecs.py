@@ -61,3 +61,23 @@ def dequant_fp8_rows(codes: np.ndarray, scales: np.ndarray, block: int = 64) -> 
     rows = np.arange(N) // block
     s = np.asarray(scales, dtype=np.float64)[..., rows]
     return vals * s[..., :, None]
+
+
+def round_to_e4m3fn(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest E4M3FN value, ties to the even code,
+    saturating at +-448; returns float64 values (not codes).
+
+    Written as a search over the decoded grid of the 127 non-negative finite
+    codes (0x00..0x7E, whose values increase with the code), so it depends on
+    nothing but ``decode_e4m3fn``.
+    """
+    grid = decode_e4m3fn(np.arange(0x7F, dtype=np.uint8))      # 0 .. 448, increasing
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), grid[-1])
+    hi = np.clip(np.searchsorted(grid, a, side="left"), 1, len(grid) - 1)
+    lo = hi - 1
+    d_lo = a - grid[lo]
+    d_hi = grid[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    r = np.where(pick_hi, grid[hi], grid[lo])
+    return np.where(np.signbit(x), -r, r)

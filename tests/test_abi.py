@@ -72,6 +72,13 @@ def test_fwd_ex_rejects(lib):
     p.q_scale = p.k_scale = p.v_scale = A
     p.d = 64
     assert lib.fa_fwd_ex(ctypes.byref(p)) == fa.FA_ERR_UNSUPPORTED      # fp8 needs d=128
+    p.d = 128
+    p.out_dtype = fa.FA_FP32
+    assert lib.fa_fwd_ex(ctypes.byref(p)) == fa.FA_ERR_UNSUPPORTED      # fp8 writes bf16 only
+    p.out_dtype = fa.FA_BF16
+    p.k_scale = A + 2
+    assert lib.fa_fwd_ex(ctypes.byref(p)) == fa.FA_ERR_INVALID_ARG      # misaligned scales
+    p.k_scale = A
     p.in_dtype = fa.FA_BF16
     p.d = 128
     assert lib.fa_fwd_ex(ctypes.byref(p)) == fa.FA_ERR_INVALID_ARG      # scales with bf16

@@ -1,0 +1,144 @@
+"""GPU parity of the block-scaled fp8 (E4M3FN) forward pass.
+
+The oracle runs on the dequantised inputs (code value times block scale, in
+float64).  Gates, stated for a kernel that rounds the probabilities to
+E4M3FN before the P*V product:
+  F1  LSE relative error <= 1e-3 (denominator max(|LSE|, 1));
+  F2  every output element within the oracle's elementwise bound
+      ``oracle.fp8_p_error_bound``, evaluated with the smallest pre-scale the
+      kernel applies to P in that head (256 * min s_v / max s_v);
+  F3  mean-abs error <= 1.25 x (the mean-abs error of
+      ``oracle.fp8_p_attention``, exact attention with only P rounded to
+      E4M3FN with the kernel's documented pre-scale) + 1e-4, over the sampled
+      rows of the full-size workload (B=4, H=16, N=8192): the kernel adds
+      little beyond the rounding of P that the fp8 product implies.  On the
+      small edge shapes, where a mean over few elements is noisy, it is
+      reported, not gated.
+The max-abs error is printed beside them.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fa_inputs as fi
+import oracle
+from _gpu_util import dev_to_f64, lse_rel, say, u8_to_dev
+
+pytestmark = pytest.mark.gpu
+
+F3_FACTOR = 1.25
+F3_SLACK = 1e-4
+LSE_REL = 1e-3
+
+
+def run_fp8(fa, codes, scales, B, H, N, d, scale, causal):
+    q, k, v = (u8_to_dev(c) for c in codes)
+    qs, ks, vs = (torch.from_numpy(np.ascontiguousarray(s)).cuda() for s in scales)
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    fa.fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, in_dtype=fa.FA_FP8_E4M3,
+                 q_scale=qs, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    return dev_to_f64(o), dev_to_f64(lse)
+
+
+def p_prescale_min(v_scales_head):
+    s = np.asarray(v_scales_head, np.float64)
+    return 256.0 * s.min() / s.max()
+
+
+def p_prescale_per_key(v_scales_head, Nk):
+    """The pre-scale the kernel documents for key j: 256 * s_v(j // 64) / max s_v."""
+    s = np.asarray(v_scales_head, np.float64)
+    return (256.0 * s / s.max())[np.arange(Nk) // 64]
+
+
+def check_head(og, lg, q, k, v, vsc, scale, causal, rows, what):
+    O, L, Bnd = oracle.fp8_p_error_bound(q[rows], k, v, scale, causal, p_prescale_min(vsc),
+                                         qidx=rows)
+    Om = oracle.fp8_p_attention(q[rows], k, v, scale, causal, p_prescale_per_key(vsc, k.shape[0]),
+                                qidx=rows)
+    err = np.abs(og - O)
+    err_model = np.abs(Om - O)
+    lr = lse_rel(lg, L)
+    ratio = float((err / Bnd).max())
+    say(f"  {what}: max_abs={err.max():.3e} mean_abs={err.mean():.3e} "
+        f"(P-rounding model {err_model.mean():.3e}) lse_rel={lr.max():.3e} "
+        f"max err/bound={ratio:.3f}")
+    assert np.all(np.isfinite(og)), f"{what}: non-finite output"
+    assert lr.max() <= LSE_REL, f"{what}: LSE relative {lr.max()}"
+    assert np.all(err <= Bnd), f"{what}: error above the fp8 bound (ratio {ratio})"
+    return err, err_model
+
+
+def gen(wid, B, H, N, d, outlier_p=1e-3):
+    codes, scales = [], []
+    for t in (fi.Q_ID, fi.K_ID, fi.V_ID):
+        c, s = fi.fp8_tensor(wid, t, B, H, N, d, outlier_p=outlier_p)
+        codes.append(c)
+        scales.append(s)
+    return codes, scales
+
+
+def test_fp8_code_semantics(gpu_lib):
+    """One key: LSE is the single score, so code 0x7E (448) times code 0x38
+    (1.0) at d = 0 must give scale * 448 exactly; O is that key's value row."""
+    fa = gpu_lib
+    B, H, N, d = 1, 1, 1, 128
+    say("fp8 code semantics: 0x7E -> 448")
+    q = np.zeros((B, H, N, d), np.uint8)
+    k = np.zeros((B, H, N, d), np.uint8)
+    q[0, 0, 0, 0] = 0x7E
+    k[0, 0, 0, 0] = 0x38
+    v = (np.arange(d, dtype=np.int64) % 120 + 1).astype(np.uint8).reshape(B, H, N, d)
+    one = np.ones((B, H, 1), np.float32)
+    scale = 0.125
+    og, lg = run_fp8(fa, (q, k, v), (one, one, one), B, H, N, d, scale, False)
+    assert abs(lg[0, 0, 0] - 448 * scale) <= 1e-5 * 448 * scale, lg[0, 0, 0]
+    ref = oracle.decode_e4m3fn(v)
+    assert np.array_equal(og, ref), (og[0, 0, 0, :8], ref[0, 0, 0, :8])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 2, 33, 64, 65, 127, 128, 200, 257, 640])
+def test_fp8_edge_shapes(gpu_lib, N, causal):
+    fa = gpu_lib
+    B, H, d = 2, 3, 128
+    wid = 5000 + 4 * N + causal
+    say(f"fp8 edge B={B} H={H} N={N} causal={causal} seed-id={wid}")
+    codes, scales = gen(wid, B, H, N, d, outlier_p=1e-2)
+    og, lg = run_fp8(fa, codes, scales, B, H, N, d, d ** -0.5, causal)
+    deq = [oracle.dequant_fp8_rows(c, s) for c, s in zip(codes, scales)]
+    errs = []
+    for b in range(B):
+        for h in range(H):
+            errs.append(check_head(og[b, h], lg[b, h], deq[0][b, h], deq[1][b, h], deq[2][b, h],
+                                   scales[2][b, h], d ** -0.5, causal, np.arange(N),
+                                   f"(b={b},h={h})"))
+    # F3 is a gate on the long rows of the measured workload; rows of a few
+    # keys carry the full 2^-4 rounding of P, so here it is only reported.
+    mean = float(np.mean(np.concatenate([e.ravel() for e, _ in errs])))
+    mean_model = float(np.mean(np.concatenate([e.ravel() for _, e in errs])))
+    say(f"  mean-abs {mean:.3e} (P-rounding model {mean_model:.3e})")
+
+
+def test_fp8_full_size(gpu_lib):
+    """B=4, H=16, N=8192, d=128, causal, 0.1% x20 outliers: sampled heads and rows."""
+    fa = gpu_lib
+    w = fi.WORKLOADS[5]
+    say(f"fp8 {w.name}: generating")
+    codes, scales = gen(w.wid, w.B, w.H, w.N, w.d)
+    say("fp8 full size: running")
+    og, lg = run_fp8(fa, codes, scales, w.B, w.H, w.N, w.d, w.scale, True)
+    assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg))
+    rows = np.unique(np.r_[0:128, 4032:4160, 8064:8192,
+                           np.random.default_rng(55).choice(w.N, 256, replace=False)])
+    errs = []
+    for b, h in [(0, 0), (1, 9), (3, 15)]:
+        q, k, v = (oracle.dequant_fp8_rows(c[b, h], s[b, h]) for c, s in zip(codes, scales))
+        errs.append(check_head(og[b, h, rows], lg[b, h, rows], q, k, v, scales[2][b, h], w.scale,
+                               True, rows, f"(b={b},h={h}) rows={len(rows)}"))
+    mean = float(np.mean(np.concatenate([e.ravel() for e, _ in errs])))
+    mean_model = float(np.mean(np.concatenate([e.ravel() for _, e in errs])))
+    say(f"  mean-abs over the sampled rows: {mean:.3e}; P-rounding model {mean_model:.3e}")
+    assert mean <= F3_FACTOR * mean_model + F3_SLACK, (mean, mean_model)

@@ -331,3 +331,100 @@ def test_fp8_bound_holds_and_is_tight(rounded, sigma):
     assert np.all(err <= Bnd)
     # tight to within a small factor somewhere (the bound is not vacuous)
     assert np.max(err / Bnd) > 0.05
+
+
+# ---------------------------------------------------------------------------
+# E4M3FN rounding and attention with E4M3FN-rounded P
+# ---------------------------------------------------------------------------
+
+def _e4m3_grid():
+    return [float(x) for x in oracle.decode_e4m3fn(np.arange(0x7F, dtype=np.uint8))]
+
+
+def test_round_e4m3fn_grid_points_and_ties():
+    grid = np.array(_e4m3_grid())
+    assert np.array_equal(oracle.round_to_e4m3fn(grid), grid)
+    assert np.array_equal(oracle.round_to_e4m3fn(-grid[1:]), -grid[1:])
+    mid = (grid[:-1] + grid[1:]) / 2
+    r = oracle.round_to_e4m3fn(mid)
+    even = np.where(np.arange(len(mid)) % 2 == 0, grid[:-1], grid[1:])   # the even code wins
+    assert np.array_equal(r, even)
+    eps = 1e-9 * np.maximum(mid, 1e-3)
+    assert np.array_equal(oracle.round_to_e4m3fn(mid - eps), grid[:-1])
+    assert np.array_equal(oracle.round_to_e4m3fn(mid + eps), grid[1:])
+    assert oracle.round_to_e4m3fn(np.array([1000.0, -500.0, 464.0])).tolist() == [448.0, -448.0, 448.0]
+
+
+def test_round_e4m3fn_agrees_with_the_input_quantiser():
+    # two independently written encoders: grid search here, frexp arithmetic there
+    from fa_inputs import f64_to_e4m3fn_codes
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-4, 3, 20000),
+                        rng.uniform(-448, 448, 5000)])
+    a = oracle.round_to_e4m3fn(x)
+    b = oracle.decode_e4m3fn(f64_to_e4m3fn_codes(x))
+    assert np.array_equal(np.abs(a), np.abs(b))
+
+
+def _brute_fp8_p(q, k, v, scale, causal, sig):
+    grid = _e4m3_grid()
+
+    def rnd(x):
+        best = min(range(len(grid)), key=lambda i: (abs(x - grid[i]), i % 2))
+        return grid[best]
+    out = []
+    for i in range(len(q)):
+        keys = [j for j in range(len(k)) if not causal or j <= i]
+        s = {j: scale * math.fsum(q[i][c] * k[j][c] for c in range(len(q[i]))) for j in keys}
+        m = max(s.values())
+        p = {j: math.exp(s[j] - m) for j in keys}
+        l = math.fsum(p.values())
+        out.append([math.fsum(rnd(p[j] * sig[j]) / sig[j] * v[j][c] for j in keys) / l
+                    for c in range(len(v[0]))])
+    return np.array(out)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_p_attention_brute_force(causal):
+    rng = np.random.default_rng(23)
+    N, d = 7, 3
+    q, k, v = _rand(rng, N, d) * 2, _rand(rng, N, d) * 2, _rand(rng, N, d)
+    sig = rng.uniform(4, 256, N)
+    O = oracle.fp8_p_attention(q, k, v, 0.5, causal, sig)
+    np.testing.assert_allclose(O, _brute_fp8_p(q, k, v, 0.5, causal, sig), rtol=0, atol=1e-12)
+
+
+def test_fp8_p_attention_exact_when_weights_are_representable():
+    # s_j = -j ln 2, so p_j = 2^-j: every weight is an E4M3FN value (down to
+    # the subnormal 2^-9), and the rounded model equals exact attention
+    N, d = 10, 4
+    q = np.zeros((1, d))
+    q[0, 0] = 1.0
+    k = np.zeros((N, d))
+    k[:, 0] = -np.arange(N) * math.log(2.0)
+    v = np.random.default_rng(3).standard_normal((N, d))
+    O = oracle.fp8_p_attention(q, k, v, 1.0, False, np.ones(N))
+    Oref, _ = attention(q, k, v, 1.0, False)
+    np.testing.assert_allclose(O, Oref, rtol=0, atol=1e-15)
+    # weights 2^-e with a pre-scale of 2^-6: e <= 3 lands on 2^-6..2^-9 (still
+    # E4M3FN values); e >= 5 lands at or below 2^-11, under half the smallest
+    # subnormal, and rounds to 0 -- those keys, and only they, drop out
+    e = np.array([0, 1, 2, 3, 5, 6, 7, 8])
+    k2 = np.zeros((len(e), d))
+    k2[:, 0] = -e * math.log(2.0)
+    v2 = v[:len(e)]
+    O2 = oracle.fp8_p_attention(q, k2, v2, 1.0, False, np.full(len(e), 2.0 ** -6))
+    p = 2.0 ** -e
+    np.testing.assert_allclose(O2[0], (p * (e <= 3)) @ v2 / p.sum(), rtol=0, atol=1e-15)
+
+
+def test_fp8_p_attention_within_the_fp8_bound():
+    rng = np.random.default_rng(29)
+    N, d = 200, 16
+    q, k, v = _rand(rng, N, d) * 2, _rand(rng, N, d) * 2, _rand(rng, N, d)
+    v[rng.random(v.shape) < 0.02] *= 20
+    sig = np.full(N, 37.0)
+    O, _, Bnd = oracle.fp8_p_error_bound(q, k, v, 0.25, True, 37.0)
+    Om = oracle.fp8_p_attention(q, k, v, 0.25, True, sig)
+    assert np.all(np.abs(Om - O) <= Bnd)
+    assert np.abs(Om - O).max() > 0          # the rounding is really applied
