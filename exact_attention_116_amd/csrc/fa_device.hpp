@@ -78,6 +78,17 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
 __device__ __forceinline__ float bf16lo(uint32_t w) { return as_f32(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return as_f32(w & 0xFFFF0000u); }
 
+// Buffer resource over [base, base + bytes): loads past the end return 0,
+// which is how the kernels read tiles that overhang the sequence without a
+// branch.  Offsets are 32-bit byte offsets from base.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 // Round two floats to bf16 (nearest even) and pack them (a in the low half).
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   bf16x2 p = {(bf16)a, (bf16)b};

@@ -19,10 +19,13 @@
 //  * P^T, rounded to bf16, is used directly as the B operand of
 //    O^T = V^T * P^T; the output accumulator O^T again has one query per
 //    lane, so the per-query rescale is a per-lane scalar.
-//  * K tiles are stored row-major in LDS; V tiles are stored transposed
-//    (V^T, d-major) with the keys permuted to match the order in which the
-//    score accumulator hands P^T to the next MFMA.  Both are double-buffered:
-//    the global loads of tile j+1 are in flight while tile j is computed.
+//  * A workgroup is 8 waves (256 queries, two waves per SIMD) sharing each
+//    K/V tile.  K tiles are stored row-major in LDS; V tiles are stored
+//    transposed (V^T, d-major) with the keys permuted to match the order in
+//    which the score accumulator hands P^T to the next MFMA.  Both are
+//    double-buffered: the global loads of tile j+1 are in flight while tile
+//    j is computed.  Loads go through buffer resources over the head, so
+//    tile rows past N read as 0 with no branch and no 64-bit address math.
 //  * Softmax runs in base 2 with scale*log2(e) folded into one FMA.  The
 //    reference max is only moved (and O, l rescaled) when some lane's max
 //    grows by more than 2^8; otherwise the stale reference is kept, which
@@ -52,8 +55,7 @@ struct FwdCfg {
   static constexpr int KCH = BC * D / 8;           // 16-byte chunks per K tile
   static constexpr int KIT = (KCH + NT - 1) / NT;  // chunks per thread
   static constexpr int VU = (BC / 4) * (D / 8);    // (4 keys x 8 d) units per V tile
-  static constexpr int VIT = (VU + NT - 1) / NT;
-  static_assert(BC % 32 == 0 && D % 32 == 0, "tile shapes");
+    static_assert(BC % 32 == 0 && D % 32 == 0, "tile shapes");
 };
 
 // Position (in 4-key groups) of key group kg inside a V^T row.  Within each
@@ -92,44 +94,33 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int qw = q0 + wave * 32;   // first query of this wave
   const int my_q = qw + l32;       // the query this lane's columns belong to
 
-  // ---- Q^T as the B operand, resident for the whole key loop ----
+  const uint32_t head_bytes = (uint32_t)N * D * 2u;
+  const rsrc_t Qr = make_rsrc(Qh, head_bytes);
+  const rsrc_t Kr = make_rsrc(Kh, head_bytes);
+  const rsrc_t Vr = make_rsrc(Vh, head_bytes);
   bf16x8 qb[D / 16];
 #pragma unroll
-  for (int u = 0; u < D / 16; ++u) {
-    if (my_q < N)
-      qb[u] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)my_q * D + 16 * u + 8 * g);
-    else
-      qb[u] = bf16x8{};
-  }
+  for (int u = 0; u < D / 16; ++u)
+    qb[u] = __builtin_bit_cast(bf16x8, buf_load16(Qr, ((uint32_t)my_q * D + 16 * u + 8 * g) * 2u));
 
   const int kv_end = CAUSAL ? min(N, q0 + C::BR) : N;
   const int ntiles = (kv_end + BC - 1) / BC;
 
-  // ---- global -> register staging of one K/V tile ----
+  static_assert(C::KCH % C::NT == 0 && C::VU % 64 == 0, "tile shapes");
+  const uint32_t k_off = (uint32_t)tid * 16u;
+  const int v_kg = tid % (BC / 4), v_dc = tid / (BC / 4);
+  const uint32_t v_off = (uint32_t)(4 * v_kg * D + 8 * v_dc) * 2u;
+  const bool v_unit = tid < C::VU;
   u32x4 kreg[C::KIT];
-  u32x4 vreg[C::VIT][4];
+  u32x4 vreg[4];
   auto load_tile = [&](int j) {
-    const int kb = j * BC;
+    const uint32_t tile = (uint32_t)j * BC * D * 2u;
 #pragma unroll
-    for (int it = 0; it < C::KIT; ++it) {
-      const int ch = it * C::NT + tid;
-      const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      const int key = kb + row;
-      kreg[it] = (ch < C::KCH && key < N)
-                     ? *reinterpret_cast<const u32x4*>(Kh + (size_t)key * D + col)
-                     : u32x4{0, 0, 0, 0};
-    }
+    for (int it = 0; it < C::KIT; ++it)
+      kreg[it] = buf_load16(Kr, tile + k_off + (uint32_t)(it * C::NT * 16));
+    if (v_unit) {
 #pragma unroll
-    for (int it = 0; it < C::VIT; ++it) {
-      const int un = it * C::NT + tid;
-      const int kg = un % (BC / 4), dc = un / (BC / 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kb + 4 * kg + r;
-        vreg[it][r] = (un < C::VU && key < N)
-                          ? *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + 8 * dc)
-                          : u32x4{0, 0, 0, 0};
-      }
+      for (int r = 0; r < 4; ++r) vreg[r] = buf_load16(Vr, tile + v_off + (uint32_t)(r * D * 2));
     }
   };
   auto store_tile = [&](int buf) {
@@ -138,26 +129,18 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
     for (int it = 0; it < C::KIT; ++it) {
       const int ch = it * C::NT + tid;
-      if (ch < C::KCH) {
-        const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-        *reinterpret_cast<u32x4*>(Ks + row * C::KST + col) = kreg[it];
-      }
+      const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
+      *reinterpret_cast<u32x4*>(Ks + row * C::KST + col) = kreg[it];
     }
+    if (v_unit) {
+      const int pos = 4 * vt_group_pos(v_kg);
 #pragma unroll
-    for (int it = 0; it < C::VIT; ++it) {
-      const int un = it * C::NT + tid;
-      if (un < C::VU) {
-        const int kg = un % (BC / 4), dc = un / (BC / 4);
-        const int pos = 4 * vt_group_pos(kg);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int w = e >> 1;
-          // keys 4kg..4kg+3 of column d = 8dc+e, as two bf16 pairs
-          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-          const uint32_t p01 = __builtin_amdgcn_perm(vreg[it][1][w], vreg[it][0][w], sel);
-          const uint32_t p23 = __builtin_amdgcn_perm(vreg[it][3][w], vreg[it][2][w], sel);
-          *reinterpret_cast<u32x2*>(Vs + (8 * dc + e) * C::VST + pos) = u32x2{p01, p23};
-        }
+      for (int e = 0; e < 8; ++e) {
+        const int w = e >> 1;
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t p01 = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel);
+        const uint32_t p23 = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], sel);
+        *reinterpret_cast<u32x2*>(Vs + (8 * v_dc + e) * C::VST + pos) = u32x2{p01, p23};
       }
     }
   };
@@ -297,7 +280,7 @@ static hipError_t launch(const FwdArgs& a) {
 
 template <int D, bool CAUSAL, bool OUT_F32>
 static hipError_t launch_d(const FwdArgs& a) {
-  return launch<D, 64, 4, CAUSAL, OUT_F32>(a);
+  return launch<D, 64, 8, CAUSAL, OUT_F32>(a);
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
