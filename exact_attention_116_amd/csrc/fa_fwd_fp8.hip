@@ -24,6 +24,8 @@
 //  * The running max is moved only when it would grow by more than 0.75 (base
 //    2), so every weight times sigma_t stays below 256 * 2^0.75 < 448, the
 //    largest E4M3FN value; skipped rescales leave the result exact.
+//  * K/V/Q codes are read through buffer resources over the head, so tile
+//    rows past N read as 0 with no per-load branch.
 //  * The contraction order over d (for S) and over keys (for P*V) is a
 //    bijection chosen so that each lane reads 32 contiguous bytes; A and B
 //    operands of one product always use the same order, so the products are
@@ -101,43 +103,45 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict_
   const int my_q = qw + l32;
   const float sq = (qw < N) ? qsh[qw >> 6] : 1.f;
 
+  // Q, K and V codes of this head through buffer resources: rows past N read 0
+  const uint32_t head_bytes = (uint32_t)N * D;
+  const rsrc_t Qr = make_rsrc(Qh, head_bytes);
+  const rsrc_t Kr = make_rsrc(Kh, head_bytes);
+  const rsrc_t Vr = make_rsrc(Vh, head_bytes);
+
   // Q codes as the B operand: lane (query my_q, half g), step u holds
   // d = 64u + 32g .. 64u + 32g + 31.
   i32x8 qb[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    if (my_q < N) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(Qh + (size_t)my_q * D + 64 * u + 32 * g);
-      const u32x4 lo = src[0], hi = src[1];
-      qb[u] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    } else {
-      qb[u] = i32x8{};
-    }
+    const uint32_t off = (uint32_t)my_q * D + 64 * u + 32 * g;
+    const u32x4 lo = buf_load16(Qr, off), hi = buf_load16(Qr, off + 16);
+    qb[u] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   }
 
   const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
   const int ntiles = (kv_end + BC - 1) / BC;
 
   // ---- global -> register staging of one K/V tile ----
-  u32x4 kreg[2];   // 64 rows x 128 B = 512 chunks of 16 B, 2 per thread
-  u32x2 vreg[4];   // one unit: 4 keys x 8 d
+  // K: 64 rows x 128 B = 512 chunks of 16 B, KIT per thread.  V: 256 units
+  // of 4 keys x 8 d, one for each of the first 256 threads (whole waves).
+  constexpr int KIT = BC * D / 16 / NT;
+  static_assert(KIT * NT == BC * D / 16 && (BC / 4) * (D / 8) == 256 && NT >= 256, "tile staging");
+  const uint32_t k_off = (uint32_t)tid * 16u;
+  const int kg = tid & 15, dc = (tid >> 4) & 15;
+  const uint32_t v_off = (uint32_t)(4 * kg * D + 8 * dc);
+  const bool v_unit = tid < 256;
+  u32x4 kreg[KIT];
+  u32x2 vreg[4];
   auto load_tile = [&](int j) {
-    const int kb = j * BC;
+    const uint32_t tile = (uint32_t)j * BC * D;
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int ch = it * NT + tid;
-      const int row = ch >> 3, col = (ch & 7) * 16;
-      const int key = kb + row;
-      kreg[it] = key < N ? *reinterpret_cast<const u32x4*>(Kh + (size_t)key * D + col)
-                         : u32x4{0, 0, 0, 0};
-    }
-    const int kg = tid & 15, dc = tid >> 4;
+    for (int it = 0; it < KIT; ++it) kreg[it] = buf_load16(Kr, tile + k_off + it * NT * 16);
+    if (v_unit) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = kb + 4 * kg + r;
-      vreg[r] = key < N ? *reinterpret_cast<const u32x2*>(Vh + (size_t)key * D + 8 * dc)
-                        : u32x2{0, 0};
+      for (int r = 0; r < 4; ++r)
+        vreg[r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(Vr, tile + v_off + r * D, 0, 0));
     }
   };
   // V^T row d holds the tile's 64 keys as 16 groups of 4; group kg sits at
@@ -148,28 +152,28 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict_
     uint8_t* Ks = smem + buf * (KTILE + VTILE);
     uint8_t* Vs = Ks + KTILE;
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
+    for (int it = 0; it < KIT; ++it) {
       const int ch = it * NT + tid;
-      const int row = ch >> 3, col = (ch & 7) * 16;
-      *reinterpret_cast<u32x4*>(Ks + row * KST + col) = kreg[it];
+      *reinterpret_cast<u32x4*>(Ks + (ch >> 3) * KST + (ch & 7) * 16) = kreg[it];
     }
-    const int kg = tid & 15, dc = tid >> 4;
-    const int pos = ((kg & 1) * 8 + (kg >> 1)) * 4;
+    if (v_unit) {
+      const int pos = ((kg & 1) * 8 + (kg >> 1)) * 4;
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      const uint32_t a = vreg[0][w], b = vreg[1][w], cc = vreg[2][w], dd = vreg[3][w];
-      const uint32_t ab_lo = __builtin_amdgcn_perm(b, a, 0x05010400u);    // a0 b0 a1 b1
-      const uint32_t ab_hi = __builtin_amdgcn_perm(b, a, 0x07030602u);    // a2 b2 a3 b3
-      const uint32_t cd_lo = __builtin_amdgcn_perm(dd, cc, 0x05010400u);  // c0 d0 c1 d1
-      const uint32_t cd_hi = __builtin_amdgcn_perm(dd, cc, 0x07030602u);  // c2 d2 c3 d3
-      const uint32_t col[4] = {
-          __builtin_amdgcn_perm(cd_lo, ab_lo, 0x05040100u),   // keys 0..3 of d = 8dc + 4w
-          __builtin_amdgcn_perm(cd_lo, ab_lo, 0x07060302u),   // d + 1
-          __builtin_amdgcn_perm(cd_hi, ab_hi, 0x05040100u),   // d + 2
-          __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u)};  // d + 3
+      for (int w = 0; w < 2; ++w) {
+        const uint32_t a = vreg[0][w], b = vreg[1][w], cc = vreg[2][w], dd = vreg[3][w];
+        const uint32_t ab_lo = __builtin_amdgcn_perm(b, a, 0x05010400u);    // a0 b0 a1 b1
+        const uint32_t ab_hi = __builtin_amdgcn_perm(b, a, 0x07030602u);    // a2 b2 a3 b3
+        const uint32_t cd_lo = __builtin_amdgcn_perm(dd, cc, 0x05010400u);  // c0 d0 c1 d1
+        const uint32_t cd_hi = __builtin_amdgcn_perm(dd, cc, 0x07030602u);  // c2 d2 c3 d3
+        const uint32_t col[4] = {
+            __builtin_amdgcn_perm(cd_lo, ab_lo, 0x05040100u),   // keys 0..3 of d = 8dc + 4w
+            __builtin_amdgcn_perm(cd_lo, ab_lo, 0x07060302u),   // d + 1
+            __builtin_amdgcn_perm(cd_hi, ab_hi, 0x05040100u),   // d + 2
+            __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u)};  // d + 3
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        *reinterpret_cast<uint32_t*>(Vs + (8 * dc + 4 * w + e) * VST + pos) = col[e];
+        for (int e = 0; e < 4; ++e)
+          *reinterpret_cast<uint32_t*>(Vs + (8 * dc + 4 * w + e) * VST + pos) = col[e];
+      }
     }
   };
 
