@@ -47,6 +47,10 @@ fa_status check_fwd(const fa_fwd_params* p) {
   const long long elems = (long long)p->B * p->H * p->N * p->d;
   if ((long long)p->B * p->H * ((p->N + 31) / 32) > 0x7FFFFFFFLL || elems <= 0)
     return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
+  // the kernels address one head with 32-bit byte offsets
+  const long long elem_bytes = p->in_dtype == FA_FP8_E4M3 ? 1 : 2;
+  if ((long long)p->N * p->d * elem_bytes >= (1LL << 32))
+    return fail(FA_ERR_UNSUPPORTED, "one (batch, head) slice must be smaller than 4 GiB");
   if (p->in_dtype == FA_BF16) {
     if (p->q_scale || p->k_scale || p->v_scale)
       return fail(FA_ERR_INVALID_ARG, "block scales are only accepted with FA_FP8_E4M3 inputs");
@@ -100,6 +104,10 @@ fa_status check_decode(const void* q, const void* kc, const void* vc, const void
   if (!good_scale(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "decode supports d = 64 or 128");
   if ((long long)B * H * S > 0x7FFFFFFFLL) return fail(FA_ERR_INVALID_ARG, "B*H*num_splits too large");
+  // a split is addressed with 32-bit byte offsets
+  const long long chunk = ((long long)Lkv + S - 1) / S;
+  if (chunk * d * 2 >= (1LL << 32))
+    return fail(FA_ERR_UNSUPPORTED, "one split of the KV cache must be smaller than 4 GiB");
   return FA_OK;
 }
 

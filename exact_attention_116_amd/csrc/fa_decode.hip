@@ -10,7 +10,9 @@
 // FlashAttention-3 snippets).
 //
 // gfx950 mapping: this is a streaming read of the whole cache, bound by
-// HBM bandwidth, not by arithmetic, so it uses no MFMA.  d/8 lanes share one
+// HBM bandwidth, not by arithmetic, so it uses no MFMA.  Each thread keeps
+// 16 K and 16 V rows (16 bytes each) in flight, read with the non-temporal
+// cache hint since every byte is used exactly once.  d/8 lanes share one
 // key row (16-byte loads, each wave instruction reads 64 x 16 B of
 // consecutive rows), the dot products use v_dot2_f32_bf16 plus a DPP
 // reduction inside the lane group, and every lane group keeps its own
@@ -43,9 +45,13 @@ void fa_decode_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__
   const int hi = (int)((long long)lo + chunk < Lkv ? (long long)lo + chunk : Lkv);
 
   const u32x4 qv = *reinterpret_cast<const u32x4*>(q + (size_t)bh * D + 8 * dl);
-  const size_t head = (size_t)bh * (size_t)Lkv * D;
-  const bf16* Kh = kc + head + 8 * dl;
-  const bf16* Vh = vc + head + 8 * dl;
+  // K/V rows of this split through buffer resources spanning exactly
+  // [lo, hi): rows past hi read as 0 (and are masked below).  The cache is
+  // streamed once, so the loads carry the non-temporal hint.
+  const size_t head = (size_t)bh * (size_t)Lkv * D + (size_t)lo * D;
+  const uint32_t span = (uint32_t)(hi - lo) * D * 2u;
+  const rsrc_t Kr = make_rsrc(kc + head, span);
+  const rsrc_t Vr = make_rsrc(vc + head, span);
 
   float m = kNegInf, l = 0.f;
   float acc[8];
@@ -56,14 +62,9 @@ void fa_decode_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__
     u32x4 kr[U], vr[U];
 #pragma unroll
     for (int uu = 0; uu < U; ++uu) {
-      const int key = base + uu * STEP + grp;
-      if (key < hi) {
-        kr[uu] = *reinterpret_cast<const u32x4*>(Kh + (size_t)key * D);
-        vr[uu] = *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D);
-      } else {
-        kr[uu] = u32x4{0, 0, 0, 0};
-        vr[uu] = u32x4{0, 0, 0, 0};
-      }
+      const uint32_t off = ((uint32_t)(base - lo + uu * STEP + grp) * D + 8 * dl) * 2u;
+      kr[uu] = buf_load16_nt(Kr, off);
+      vr[uu] = buf_load16_nt(Vr, off);
     }
     float sc[U];
     float mx = kNegInf;
@@ -149,7 +150,7 @@ void fa_decode_combine_kernel(const float* __restrict__ part_o, const float* __r
 
 template <int D>
 static hipError_t launch_d(const DecodeArgs& a) {
-  constexpr int NW = 4, U = 8;
+  constexpr int NW = 4, U = 16;
   const int BH = a.B * a.H;
   const int chunk = (int)(((long long)a.Lkv + a.num_splits - 1) / a.num_splits);
   hipStream_t st = (hipStream_t)a.stream;

@@ -89,6 +89,11 @@ __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// The same with the non-temporal hint (for data read exactly once).
+__device__ __forceinline__ u32x4 buf_load16_nt(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
+
 // Round two floats to bf16 (nearest even) and pack them (a in the low half).
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   bf16x2 p = {(bf16)a, (bf16)b};

@@ -57,6 +57,8 @@ typedef enum {
  * q, k, v : bf16 [B, H, N, d]      o : bf16 [B, H, N, d]
  * lse     : fp32 [B, H, N]         (natural-log log-sum-exp of the scaled scores)
  * d in {64, 128}; N >= 1 (any length; tails are masked); B, H >= 1;
+ * one (b, h) slice of q/k/v must be under 4 GiB (N * d * 2 < 2^32), else
+ * FA_ERR_UNSUPPORTED;
  * scale finite and > 0 (the usual value is 1/sqrt(d), the softmax_scale
  * default of the flash_attn_func call in the note's "框架集成" section);
  * causal != 0 masks key j > query i (the causal=True option of the note's
@@ -115,6 +117,7 @@ fa_status fa_fwd_ex(const fa_fwd_params* p);
  * kcache, vcache : bf16 [B, H, Lkv, d]   (no mask; every key is visible)
  * num_splits in [1, Lkv]: split s covers keys [s*c, min((s+1)*c, Lkv)),
  * c = ceil(Lkv / num_splits).  scale = 1/sqrt(d).  d in {64, 128}.
+ * One split must span under 4 GiB (c * d * 2 < 2^32), else FA_ERR_UNSUPPORTED.
  * Each split writes a normalised partial O_s and its LSE_s (fp32) to a
  * workspace; a second kernel merges them with weights exp(LSE_s - LSE).
  * The workspace is owned by the library, grown on demand per device and

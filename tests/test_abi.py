@@ -58,6 +58,7 @@ def _fwd(lib, q=A, k=A, v=A, o=A, lse=A, B=1, H=1, N=16, d=128, scale=0.1, causa
     (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=1 << 24), fa.FA_ERR_UNSUPPORTED),      # a 4 GiB head: beyond 32-bit offsets
 ])
 def test_fwd_rejects(lib, kw, status):
     assert _fwd(lib, **kw) == status
@@ -107,6 +108,7 @@ def test_workspace_bytes(lib):
     (dict(d=80), fa.FA_ERR_UNSUPPORTED),
     (dict(ws=None), fa.FA_ERR_WORKSPACE),
     (dict(ws_bytes=100), fa.FA_ERR_WORKSPACE),
+    (dict(Lkv=1 << 24, S=1), fa.FA_ERR_UNSUPPORTED),   # a 4 GiB split
 ])
 def test_decode_ex_rejects(lib, kw, status):
     a = dict(q=A, kc=A, vc=A, o=A, lse=None, B=1, H=2, Lkv=16, d=128, S=4, scale=0.1,
