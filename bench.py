@@ -28,6 +28,37 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 
 PEAK_FP8_TFLOPS = 5033.2      # dense fp8
 PEAK_HBM_GBS = 8000.0
 
+# HBM bytes per launch, from rocprofv3 counter runs (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch, averaged over the dispatches of
+# `bench.py --only <w> --steps 2 --warmup 1 --copy-calibration`).  The same
+# counters read a 1 GiB device copy as 524300 KiB fetched and 1048576 KiB
+# written, so fetches are scaled by 1048576/524300 and writes by 1.  Each
+# entry is tied to the SHA-256 of its kernel source plus the shared device
+# header: once either changes, the figure no longer describes the kernel and
+# the bench reports traffic as null.
+COUNTER_SCALE = {"fetch": 1048576.0 / 524300.0, "write": 1.0}
+TRAFFIC_KIB = {
+    "c3": {"src": "fa_fwd_bf16.hip", "fetch_kib": 257931.0, "write_kib": 66565.0,
+           "sha256": "27e8bfa77a7813835e299e13346fb79f23947319b72b4ec1fdc49338b9dcb7d6"},
+    "c4": {"src": "fa_decode.hip", "fetch_kib": 4194676.0 + 4172.0, "write_kib": 8706.0 + 72.0,
+           "sha256": "fb3ef4135af8a9afb791ad62ee1419918618a3d14c4d8501b91f2dcfc12190ec"},
+}
+
+
+def traffic_bytes(workload):
+    """Counter-measured HBM bytes per launch, or None if the kernel changed."""
+    import hashlib
+    t = TRAFFIC_KIB.get(workload)
+    if t is None:
+        return None
+    csrc = os.path.join(ROOT, "exact_attention_116_amd", "csrc")
+    with open(os.path.join(csrc, t["src"]), "rb") as f, \
+            open(os.path.join(csrc, "fa_device.hpp"), "rb") as g:
+        digest = hashlib.sha256(f.read() + g.read()).hexdigest()
+    if digest != t["sha256"]:
+        return None
+    return 1024.0 * (t["fetch_kib"] * COUNTER_SCALE["fetch"] + t["write_kib"] * COUNTER_SCALE["write"])
+
 
 def fwd_flops(w, causal):
     f = 4.0 * w.B * w.H * w.N * w.N * w.d
@@ -100,9 +131,10 @@ def cpu_baseline(seconds):
         "unit": "TFLOPS",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"fp64 two-pass oracle, causal B=2 H=32 N=2048 d=128: {heads} of 64 heads "
-                   f"in {t_fwd:.1f} s (input generation and bf16 decoding included); "
-                   f"decode oracle B=8 H=32 Lkv=65536 d=128: {pairs} (b,h) pairs in {t_dec:.1f} s"),
+        "sample": (f"fp64 two-pass oracle on (b,h) heads of causal B=2 H=32 N=2048 d=128, "
+                   f"cycling over the 64 heads: {heads} head evaluations in {t_fwd:.1f} s "
+                   f"(input generation and bf16 decoding included); decode oracle on (b,h) "
+                   f"pairs of B=8 H=32 Lkv=65536 d=128: {pairs} pairs in {t_dec:.1f} s"),
         "decode_value": nbytes / t_dec / 1e9,
         "decode_unit": "GB/s",
         "cpu_model": cpu_info(),
@@ -259,14 +291,17 @@ def main():
         pk = PEAK_FP8_TFLOPS if res[dom]["kind"] == "fwd_fp8" else PEAK_BF16_TFLOPS
         a = res[dom]["tflops"]
         roof = {"kernel": f"fa_fwd_bf16_kernel ({dom})", "bound": "mfma", "achieved": a,
-                "peak": pk, "unit": "TFLOP/s", "frac": a / pk, "traffic": None}
+                "peak": pk, "unit": "TFLOP/s", "frac": a / pk, "traffic": traffic_bytes(dom),
+                "algorithmic_bytes": res[dom]["bytes"]}
     decode = None
     if "c4" in res:
         g = res["c4"]["gbs"]
         decode = {"value": g, "unit": "GB/s", "ms": res["c4"]["ms_mean"],
                   "roofline": {"kernel": "fa_decode_split_kernel + fa_decode_combine_kernel",
                                "bound": "hbm", "achieved": g, "peak": PEAK_HBM_GBS,
-                               "unit": "GB/s", "frac": g / PEAK_HBM_GBS, "traffic": None}}
+                               "unit": "GB/s", "frac": g / PEAK_HBM_GBS,
+                               "traffic": traffic_bytes("c4"),
+                               "algorithmic_bytes": res["c4"]["bytes"]}}
     prop = torch.cuda.get_device_properties(0)
     out = {
         "metric": METRIC,
