@@ -92,3 +92,29 @@ def test_decode_full_size(gpu_lib):
     o1, lse1, _, _ = run_ex(fa, q, k, v, w.B, w.H, w.Lkv, w.d, 1, w.scale)
     assert np.abs(dev_to_f64(o1) - og).max() <= 1e-2
     assert np.abs(dev_to_f64(lse1) - lg).max() <= 1e-3
+
+
+def test_decode_deterministic_and_in_bounds(gpu_lib):
+    """Two runs give identical bits; guard bands around o, lse and the
+    workspace stay untouched (a workspace larger than needed)."""
+    fa = gpu_lib
+    B, H, Lkv, d, S = 2, 3, 5000, 128, 9
+    say("decode determinism + guard bands")
+    qb, kb, vb = gen(4700, B, H, Lkv, d)
+    q, k, v = map(bf16_to_dev, (qb, kb, vb))
+    G = 4096
+    nel = B * H * d
+    obuf = torch.full((nel + 2 * G,), 7.0, dtype=torch.bfloat16, device="cuda")
+    lbuf = torch.full((B * H + 2 * G,), 7.0, dtype=torch.float32, device="cuda")
+    need = fa.fa_decode_workspace_bytes(B, H, d, S)
+    wbuf = torch.full((need // 4 + 2 * G,), 7.0, dtype=torch.float32, device="cuda")
+    outs = []
+    for _ in range(2):
+        fa.fa_decode_splitkv_ex(q, k, v, obuf[G:G + nel], lbuf[G:G + B * H], B, H, Lkv, d, S,
+                                d ** -0.5, wbuf[G:G + need // 4], need)
+        torch.cuda.synchronize()
+        outs.append((obuf[G:G + nel].clone(), lbuf[G:G + B * H].clone()))
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert torch.equal(outs[0][1], outs[1][1])
+    for buf, n in ((obuf, nel), (lbuf, B * H), (wbuf, need // 4)):
+        assert torch.all(buf[:G] == 7.0) and torch.all(buf[G + n:] == 7.0)

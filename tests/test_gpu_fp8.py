@@ -142,3 +142,27 @@ def test_fp8_full_size(gpu_lib):
     mean_model = float(np.mean(np.concatenate([e.ravel() for _, e in errs])))
     say(f"  mean-abs over the sampled rows: {mean:.3e}; P-rounding model {mean_model:.3e}")
     assert mean <= F3_FACTOR * mean_model + F3_SLACK, (mean, mean_model)
+
+
+def test_fp8_deterministic_and_in_bounds(gpu_lib):
+    """Two runs give identical bits; guard bands around o and lse stay untouched."""
+    fa = gpu_lib
+    B, H, N, d = 1, 3, 300, 128
+    say("fp8 determinism + guard bands")
+    codes, scales = gen(5900, B, H, N, d)
+    q, k, v = (u8_to_dev(c) for c in codes)
+    qs, ks, vs = (torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in scales)
+    G = 4096
+    nel = B * H * N * d
+    obuf = torch.full((nel + 2 * G,), 7.0, dtype=torch.bfloat16, device="cuda")
+    lbuf = torch.full((B * H * N + 2 * G,), 7.0, dtype=torch.float32, device="cuda")
+    outs = []
+    for _ in range(2):
+        fa.fa_fwd_ex(q, k, v, obuf[G:G + nel], lbuf[G:G + B * H * N], B, H, N, d, d ** -0.5, True,
+                     in_dtype=fa.FA_FP8_E4M3, q_scale=qs, k_scale=ks, v_scale=vs)
+        torch.cuda.synchronize()
+        outs.append((obuf[G:G + nel].clone(), lbuf[G:G + B * H * N].clone()))
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert torch.equal(outs[0][1], outs[1][1])
+    assert torch.all(obuf[:G] == 7.0) and torch.all(obuf[G + nel:] == 7.0)
+    assert torch.all(lbuf[:G] == 7.0) and torch.all(lbuf[G + B * H * N:] == 7.0)

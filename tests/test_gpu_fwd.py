@@ -43,7 +43,7 @@ def test_single_head_fp32_out(gpu_lib):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("N", [1, 2, 31, 32, 33, 64, 127, 128, 129, 200, 257, 640])
+@pytest.mark.parametrize("N", [1, 2, 31, 32, 33, 64, 127, 128, 129, 200, 255, 256, 257, 511, 640, 1000])
 def test_edge_shapes(gpu_lib, N, causal, d):
     fa = gpu_lib
     B, H = 2, 3
