@@ -20,12 +20,17 @@
 //    O^T = V^T * P^T; the output accumulator O^T again has one query per
 //    lane, so the per-query rescale is a per-lane scalar.
 //  * A workgroup is 8 waves (256 queries, two waves per SIMD) sharing each
-//    K/V tile.  K tiles are stored row-major in LDS; V tiles are stored
-//    transposed (V^T, d-major) with the keys permuted to match the order in
-//    which the score accumulator hands P^T to the next MFMA.  Both are
-//    double-buffered: the global loads of tile j+1 are in flight while tile
-//    j is computed.  Loads go through buffer resources over the head, so
-//    tile rows past N read as 0 with no branch and no 64-bit address math.
+//    128-key K/V tile, double-buffered in LDS.  Tiles move from HBM to LDS
+//    with direct buffer loads (no register staging, no LDS store
+//    instructions), issued for tile j+1 while tile j is computed; rows past
+//    N read as 0 through the buffer resource's range.  K and V are stored
+//    row-major with the 16-byte chunks of each row XOR-swizzled (K by the
+//    row index mod 16, V by twice the row index mod 4) so that the MFMA
+//    operand reads hit distinct LDS banks.  V^T operands are read with the
+//    transposing ds_read_b64_tr_b16: lane j of each 16-lane group points at
+//    one key row and four columns, and lane i receives one column over four
+//    consecutive keys -- the order in which the score accumulator hands P^T
+//    to the next MFMA.
 //  * Softmax runs in base 2 with scale*log2(e) folded into one FMA.  The
 //    reference max is only moved (and O, l rescaled) when some lane's max
 //    grows by more than 2^8; otherwise the stale reference is kept, which
@@ -48,25 +53,12 @@ template <int D, int BC, int NW>
 struct FwdCfg {
   static constexpr int NT = NW * 64;
   static constexpr int BR = NW * 32;       // queries per workgroup
-  static constexpr int KST = D + 8;        // K row stride in LDS (bf16 elements)
-  static constexpr int VST = BC + 8;       // V^T row stride in LDS
+  static constexpr int KST = D;            // K row stride in LDS (bf16), unpadded
+  static constexpr int VST = D;            // V row stride in LDS (bf16), unpadded
   static constexpr int KTILE = BC * KST;
-  static constexpr int VTILE = D * VST;
-  static constexpr int KCH = BC * D / 8;           // 16-byte chunks per K tile
-  static constexpr int KIT = (KCH + NT - 1) / NT;  // chunks per thread
-  static constexpr int VU = (BC / 4) * (D / 8);    // (4 keys x 8 d) units per V tile
-    static_assert(BC % 32 == 0 && D % 32 == 0, "tile shapes");
+  static constexpr int VTILE = BC * VST;
+  static_assert(BC % 32 == 0 && D % 32 == 0, "tile shapes");
 };
-
-// Position (in 4-key groups) of key group kg inside a V^T row.  Within each
-// 32-key block the score accumulator of lane half h holds key groups
-// {h, h+2} for the first 16-key MFMA step and {4+h, 6+h} for the second;
-// swapping bits 0 and 1 of the group index makes each of those a
-// contiguous 8-key run, readable with one 16-byte LDS load.
-__device__ __forceinline__ int vt_group_pos(int kg) {
-  const int g = kg & 7;
-  return (kg & ~7) | (g & 4) | ((g & 1) << 1) | ((g >> 1) & 1);
-}
 
 template <int D, int BC, int NW, bool CAUSAL, bool OUT_F32>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
@@ -106,45 +98,57 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int kv_end = CAUSAL ? min(N, q0 + C::BR) : N;
   const int ntiles = (kv_end + BC - 1) / BC;
 
-  static_assert(C::KCH % C::NT == 0 && C::VU % 64 == 0, "tile shapes");
-  const uint32_t k_off = (uint32_t)tid * 16u;
-  const int v_kg = tid % (BC / 4), v_dc = tid / (BC / 4);
-  const uint32_t v_off = (uint32_t)(4 * v_kg * D + 8 * v_dc) * 2u;
-  const bool v_unit = tid < C::VU;
-  u32x4 kreg[C::KIT];
-  u32x4 vreg[4];
+  // Direct global -> LDS loads.  One wave instruction fills 1 KB of LDS
+  // (lane i -> bytes 16i..16i+15); the 16-byte chunk c of row r sits at
+  // chunk position c ^ (r % NCH) for K and c ^ 2(r % 4) for V, so the MFMA
+  // reads below hit distinct banks.  Each lane's global offset carries the
+  // inverse permutation.
+  constexpr int RB = D * 2;                      // bytes per row
+  constexpr int NCH = RB / 16;                   // chunks per row
+  constexpr int NI = BC * RB / 1024;             // 1 KB instructions per tile
+  constexpr int IPW = NI / NW;                   // per wave, for K and for V each
+  static_assert(NI % NW == 0 && NCH >= 8, "direct-load tiling");
+  uint32_t gk[IPW], gv[IPW];
+#pragma unroll
+  for (int x = 0; x < IPW; ++x) {
+    const int blk = wave * IPW + x;
+    const int byte = blk * 1024 + lane * 16;
+    const int r = byte / RB, p = (byte % RB) / 16;
+    gk[x] = (uint32_t)(r * RB + 16 * (p ^ (r % NCH)));
+    gv[x] = (uint32_t)(r * RB + 16 * (p ^ (2 * (r & 3))));
+  }
   auto load_tile = [&](int j) {
-    const uint32_t tile = (uint32_t)j * BC * D * 2u;
+    const uint32_t tile = (uint32_t)j * BC * RB;
+    uint8_t* Kd = reinterpret_cast<uint8_t*>(smem + (j & 1) * (C::KTILE + C::VTILE));
+    uint8_t* Vd = Kd + C::KTILE * 2;
+#if defined(__HIP_DEVICE_COMPILE__)  // the LDS-DMA builtin exists in the device pass only
 #pragma unroll
-    for (int it = 0; it < C::KIT; ++it)
-      kreg[it] = buf_load16(Kr, tile + k_off + (uint32_t)(it * C::NT * 16));
-    if (v_unit) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vreg[r] = buf_load16(Vr, tile + v_off + (uint32_t)(r * D * 2));
+    for (int x = 0; x < IPW; ++x) {
+      const int blk = wave * IPW + x;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(Kr, (__attribute__((address_space(3))) void*)(Kd + blk * 1024), 16, tile + gk[x], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(Vr, (__attribute__((address_space(3))) void*)(Vd + blk * 1024), 16, tile + gv[x], 0, 0, 0);
     }
+#endif
   };
-  auto store_tile = [&](int buf) {
-    bf16* Ks = smem + buf * (C::KTILE + C::VTILE);
-    bf16* Vs = Ks + C::KTILE;
-#pragma unroll
-    for (int it = 0; it < C::KIT; ++it) {
-      const int ch = it * C::NT + tid;
-      const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(Ks + row * C::KST + col) = kreg[it];
-    }
-    if (v_unit) {
-      const int pos = 4 * vt_group_pos(v_kg);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t p01 = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel);
-        const uint32_t p23 = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], sel);
-        *reinterpret_cast<u32x2*>(Vs + (8 * v_dc + e) * C::VST + pos) = u32x2{p01, p23};
-      }
-    }
-  };
+  auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
 
+  // per-lane LDS read offsets (bytes within a tile).  K: row l32 (+32b),
+  // logical chunk 2u + g.  V (transposing reads): lane j of a 16-lane group
+  // reads row 4g + j/4 (+16t, +8), columns 32cb + 16dh + 4(j%4), i.e.
+  // logical chunk 4cb + 2dh + (j%4)/2 and byte 8(j%2) inside it.
+  uint32_t k_rd[D / 16], v_rd[D / 32];
+#pragma unroll
+  for (int u = 0; u < D / 16; ++u)
+    k_rd[u] = (uint32_t)(l32 * RB + 16 * ((2 * u + g) ^ (l32 % NCH)));
+  {
+    const int j16 = lane & 15, dh = (lane >> 4) & 1, q4 = j16 >> 2;
+    const int r = 4 * g + q4;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) {
+      const int c = 4 * cb + 2 * dh + ((j16 & 3) >> 1);
+      v_rd[cb] = (uint32_t)(r * RB + 16 * (c ^ (2 * (r & 3))) + 8 * (j16 & 1));
+    }
+  }
   f32x16 acc[D / 32];
 #pragma unroll
   for (int cb = 0; cb < D / 32; ++cb) acc[cb] = f32x16{};
@@ -152,7 +156,7 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   float l = 0.f;       // this lane's share of the row sum (keys of its half)
 
   load_tile(0);
-  store_tile(0);
+  wait_loads();
   __syncthreads();
 
   for (int j = 0; j < ntiles; ++j) {
@@ -174,8 +178,8 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       for (int u = 0; u < D / 16; ++u) {
 #pragma unroll
         for (int b = 0; b < BC / 32; ++b) {
-          const bf16x8 ka =
-              *reinterpret_cast<const bf16x8*>(Ks + (32 * b + l32) * C::KST + 16 * u + 8 * g);
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
+              reinterpret_cast<const uint8_t*>(Ks) + (32 * b) * RB + k_rd[u]);
           s[b] = mfma32x32x16(ka, qb[u], s[b]);
         }
       }
@@ -233,14 +237,19 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       for (int t = 0; t < BC / 16; ++t) {
 #pragma unroll
         for (int cb = 0; cb < D / 32; ++cb) {
-          const bf16x8 va =
-              *reinterpret_cast<const bf16x8*>(Vs + (32 * cb + l32) * C::VST + 16 * t + 8 * g);
+          typedef short s16x4 __attribute__((ext_vector_type(4)));
+          const uint8_t* vp = reinterpret_cast<const uint8_t*>(Vs) + (16 * t) * RB + v_rd[cb];
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(vp));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(vp + 8 * RB));
+          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           acc[cb] = mfma32x32x16(va, pb[t], acc[cb]);
         }
       }
     }
 
-    if (more) store_tile(buf ^ 1);
+    if (more) wait_loads();
     __syncthreads();
   }
 
@@ -280,7 +289,7 @@ static hipError_t launch(const FwdArgs& a) {
 
 template <int D, bool CAUSAL, bool OUT_F32>
 static hipError_t launch_d(const FwdArgs& a) {
-  return launch<D, 64, 8, CAUSAL, OUT_F32>(a);
+  return launch<D, 128, 8, CAUSAL, OUT_F32>(a);
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
