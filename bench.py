@@ -38,8 +38,8 @@ PEAK_HBM_GBS = 8000.0
 # the bench reports traffic as null.
 COUNTER_SCALE = {"fetch": 1048576.0 / 524300.0, "write": 1.0}
 TRAFFIC_KIB = {
-    "c3": {"src": "fa_fwd_bf16.hip", "fetch_kib": 257931.0, "write_kib": 66565.0,
-           "sha256": "27e8bfa77a7813835e299e13346fb79f23947319b72b4ec1fdc49338b9dcb7d6"},
+    "c3": {"src": "fa_fwd_bf16.hip", "fetch_kib": 348054.0, "write_kib": 66560.0,
+           "sha256": "38787770bb54535a289b796c2b456af1c5563f69ddd552b4388e45dcfc5b3746"},
     "c4": {"src": "fa_decode.hip", "fetch_kib": 4194676.0 + 4172.0, "write_kib": 8706.0 + 72.0,
            "sha256": "fb3ef4135af8a9afb791ad62ee1419918618a3d14c4d8501b91f2dcfc12190ec"},
 }
