@@ -30,7 +30,7 @@
 //    transposing ds_read_b64_tr_b16: lane j of each 16-lane group points at
 //    one key row and four columns, and lane i receives one column over four
 //    consecutive keys -- the order in which the score accumulator hands P^T
-//    to the next MFMA.
+//    to the next MFMA.  Operand reads run four MFMAs ahead of their use.
 //  * Softmax runs in base 2 with scale*log2(e) folded into one FMA.  The
 //    reference max is only moved (and O, l rescaled) when some lane's max
 //    grows by more than 2^8; otherwise the stale reference is kept, which
@@ -174,13 +174,25 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       f32x16 s[BC / 32];
 #pragma unroll
       for (int b = 0; b < BC / 32; ++b) s[b] = f32x16{};
+      {
+        // K fragments are read PD MFMAs ahead of their use; the scheduling
+        // fence after every step keeps the compiler from sinking each read
+        // next to its MFMA (which leaves only two LDS reads in flight)
+        constexpr int PDK = 4;
+        constexpr int NB = BC / 32, NQ = (D / 16) * NB;
+        bf16x8 kf[NQ];
 #pragma unroll
-      for (int u = 0; u < D / 16; ++u) {
-#pragma unroll
-        for (int b = 0; b < BC / 32; ++b) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
-              reinterpret_cast<const uint8_t*>(Ks) + (32 * b) * RB + k_rd[u]);
-          s[b] = mfma32x32x16(ka, qb[u], s[b]);
+        for (int i = 0; i < NQ + PDK; ++i) {
+          if (i < NQ) {
+            const int u = i / NB, b = i % NB;
+            kf[i] = *reinterpret_cast<const bf16x8*>(
+                reinterpret_cast<const uint8_t*>(Ks) + (32 * b) * RB + k_rd[u]);
+          }
+          if (i >= PDK) {
+            const int x = i - PDK, u = x / NB, b = x % NB;
+            s[b] = mfma32x32x16(kf[x], qb[u], s[b]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
 
@@ -233,18 +245,28 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       }
 
       // ---- O^T += V^T * P^T ----
+      {
+        // V^T fragments, read PDV MFMAs ahead as for K
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        constexpr int PDV = 4;
+        constexpr int NC = D / 32, NV = (BC / 16) * NC;
+        bf16x8 vf[NV];
 #pragma unroll
-      for (int t = 0; t < BC / 16; ++t) {
-#pragma unroll
-        for (int cb = 0; cb < D / 32; ++cb) {
-          typedef short s16x4 __attribute__((ext_vector_type(4)));
-          const uint8_t* vp = reinterpret_cast<const uint8_t*>(Vs) + (16 * t) * RB + v_rd[cb];
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(vp));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(vp + 8 * RB));
-          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[cb] = mfma32x32x16(va, pb[t], acc[cb]);
+        for (int i = 0; i < NV + PDV; ++i) {
+          if (i < NV) {
+            const int t = i / NC, cb = i % NC;
+            const uint8_t* vp = reinterpret_cast<const uint8_t*>(Vs) + (16 * t) * RB + v_rd[cb];
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(vp));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(vp + 8 * RB));
+            vf[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+          if (i >= PDV) {
+            const int x = i - PDV, t = x / NC, cb = x % NC;
+            acc[cb] = mfma32x32x16(vf[x], pb[t], acc[cb]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
