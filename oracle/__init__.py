@@ -12,7 +12,8 @@ codecs      decode bf16 bit patterns and OCP E4M3FN codes to float64 from
 attention   the plain definition O = softmax(scale*Q*K^T)*V with its
             log-sum-exp, in float64, score matrix materialised, two passes
             (max, then exp/sum); the split-KV partials over key ranges and
-            their log-sum-exp-weighted merge; the elementwise error bound of
+            their log-sum-exp-weighted merge; single-query decode with
+            grouped key/value heads; the elementwise error bound of
             an fp8-P kernel; attention with only P rounded to E4M3FN (the
             yardstick for an fp8 kernel's mean error).
 
@@ -23,5 +24,5 @@ and closed-form invariants.  Nothing in here is "parity unpinned".
 from .codecs import decode_bf16, decode_e4m3fn, dequant_fp8_rows, round_to_e4m3fn  # noqa: F401
 from .attention import (  # noqa: F401
     attention, attention_rows, split_bounds, split_partials, merge_partials,
-    decode_attention, fp8_p_error_bound, fp8_p_attention,
+    decode_attention, decode_attention_gqa, fp8_p_error_bound, fp8_p_attention,
 )

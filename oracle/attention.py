@@ -157,6 +157,27 @@ def decode_attention(q, k, v, scale):
     return attention(q, k, v, scale, causal=False)
 
 
+def decode_attention_gqa(q, k, v, scale):
+    """Single-query decode with grouped key/value heads (GQA; MQA when there is
+    one key/value head): query head h attends over key/value head h // G,
+    G = Hq / Hkv, so consecutive query heads share a cached K/V head (CSDN,
+    "flash attention CUDA programming, pipeline-parallel acceleration V6",
+    related-post note on MQA: keys and values drop to one shared head while
+    queries keep all of theirs; GQA is the plain generalisation to Hkv heads).
+
+    q: [..., Hq, 1, d]; k, v: [..., Hkv, Lkv, d] with Hq a multiple of Hkv.
+    Returns (O [..., Hq, 1, d], LSE [..., Hq, 1]).
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    Hq, Hkv = q.shape[-3], k.shape[-3]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    kv_of = np.arange(Hq) // (Hq // Hkv)
+    return attention(q, k[..., kv_of, :, :], v[..., kv_of, :, :], scale, causal=False)
+
+
 # ---------------------------------------------------------------------------
 # fp8: the elementwise bound on an fp8-P kernel's error
 # ---------------------------------------------------------------------------

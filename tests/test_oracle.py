@@ -428,3 +428,51 @@ def test_fp8_p_attention_within_the_fp8_bound():
     Om = oracle.fp8_p_attention(q, k, v, 0.25, True, sig)
     assert np.all(np.abs(Om - O) <= Bnd)
     assert np.abs(Om - O).max() > 0          # the rounding is really applied
+
+
+# ---------------------------------------------------------------------------
+# grouped key/value heads (GQA / MQA) decode
+# ---------------------------------------------------------------------------
+
+def test_gqa_with_one_query_head_per_kv_head_is_mha():
+    rng = np.random.default_rng(31)
+    q, k, v = _rand(rng, 2, 4, 1, 8), _rand(rng, 2, 4, 50, 8), _rand(rng, 2, 4, 50, 8)
+    O, L = oracle.decode_attention_gqa(q, k, v, 0.3)
+    Om, Lm = oracle.decode_attention(q, k, v, 0.3)
+    np.testing.assert_array_equal(O, Om)
+    np.testing.assert_array_equal(L, Lm)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (6, 1), (8, 8)])
+def test_gqa_brute_force(Hq, Hkv):
+    rng = np.random.default_rng(37 + Hq + Hkv)
+    B, L, d = 2, 9, 3
+    q, k, v = _rand(rng, B, Hq, 1, d), _rand(rng, B, Hkv, L, d), _rand(rng, B, Hkv, L, d)
+    O, Ls = oracle.decode_attention_gqa(q, k, v, 0.7)
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            kh = h // G
+            s = [0.7 * math.fsum(q[b, h, 0, c] * k[b, kh, j, c] for c in range(d)) for j in range(L)]
+            mx = max(s)
+            e = [math.exp(x - mx) for x in s]
+            tot = math.fsum(e)
+            for c in range(d):
+                ref = math.fsum(e[j] * v[b, kh, j, c] for j in range(L)) / tot
+                assert abs(O[b, h, 0, c] - ref) <= 1e-12
+            assert abs(Ls[b, h, 0] - (mx + math.log(tot))) <= 1e-12
+
+
+def test_gqa_against_torch_sdpa():
+    rng = np.random.default_rng(41)
+    B, Hq, Hkv, L, d = 2, 8, 2, 200, 16
+    q, k, v = _rand(rng, B, Hq, 1, d), _rand(rng, B, Hkv, L, d), _rand(rng, B, Hkv, L, d)
+    O, _ = oracle.decode_attention_gqa(q, k, v, 0.25)
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=0.25, enable_gqa=True)
+    np.testing.assert_allclose(O, ref.numpy(), rtol=0, atol=1e-12)
+
+
+def test_gqa_rejects_uneven_groups():
+    with pytest.raises(ValueError):
+        oracle.decode_attention_gqa(np.zeros((1, 3, 1, 2)), np.zeros((1, 2, 4, 2)), np.zeros((1, 2, 4, 2)), 1.0)
