@@ -5,6 +5,8 @@ One step = one pass of the whole hot path over resident synthetic inputs:
   * bf16 forward, B=2 H=32 N=2048 d=128, causal and non-causal
   * bf16 forward, B=1 H=16 N=16384 d=128, causal
   * split-KV decode, B=8 H=32 Lkv=65536 d=128, 64 splits (split + merge kernels)
+  * split-KV decode with grouped K/V heads, B=8 Lkv=65536 d=128, 64 splits:
+    Hq=64 over Hkv=8 (GQA), and Hq=32 over one K/V head (MQA)
   * fp8 forward, B=4 H=16 N=8192 d=128, causal (when the library has it)
 
 ``value`` is the bf16 causal forward throughput over the N=2048 and N=16384
@@ -71,7 +73,9 @@ def fwd_bytes(w, in_bytes=2, out_bytes=2):
 
 
 def decode_bytes(w):
-    kv = 2 * w.B * w.H * w.Lkv * w.d * 2
+    """K and V read once, q read and o written once (bf16)."""
+    hkv = w.Hkv or w.H
+    kv = 2 * w.B * hkv * w.Lkv * w.d * 2
     return kv + 2 * w.B * w.H * w.d * 2
 
 
@@ -149,7 +153,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--only", default="all", help="all | c2c | c2n | c3 | c4 | c5 (profiling)")
+    ap.add_argument("--only", default="all",
+                    help="all | c2c | c2n | c3 | c4 | c5 | c6 | c7 (profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy per step (for HBM counter scaling)")
     args = ap.parse_args()
@@ -206,6 +211,24 @@ def main():
         jobs.append(("c4", lambda: fa.fa_decode_splitkv_ex(
             q4, k4, v4, o4, l4, w4.B, w4.H, w4.Lkv, w4.d, w4.num_splits, w4.scale, ws4, wsb,
             stream=stream), 4.0 * w4.B * w4.H * w4.Lkv * w4.d, decode_bytes(w4), "decode"))
+    for tag, wid in (("c6", 6), ("c7", 7)):
+        if not want(tag):
+            continue
+        wg = fi.WORKLOADS[wid]
+        log(f"generating grouped decode B={wg.B} Hq={wg.H} Hkv={wg.Hkv} Lkv={wg.Lkv} inputs")
+        qg = up_bf16(fi.bf16_tensor(wg.wid, 0, wg.B, wg.H, 1, wg.d))
+        kg = up_bf16(fi.bf16_tensor(wg.wid, 1, wg.B, wg.Hkv, wg.Lkv, wg.d))
+        vg = up_bf16(fi.bf16_tensor(wg.wid, 2, wg.B, wg.Hkv, wg.Lkv, wg.d))
+        og = torch.empty_like(qg)
+        lg = torch.empty((wg.B, wg.H), dtype=torch.float32, device=dev)
+        wsg_b = fa.fa_decode_workspace_bytes(wg.B, wg.H, wg.d, wg.num_splits)
+        wsg = torch.empty(wsg_b // 4, dtype=torch.float32, device=dev)
+        jobs.append((tag, (lambda w=wg, q=qg, k=kg, v=vg, o=og, l=lg, ws=wsg, nb=wsg_b:
+                           fa.fa_decode_splitkv_gqa(q, k, v, o, l, w.B, w.H, w.Hkv, w.Lkv, w.d,
+                                                    w.num_splits, w.scale, ws, nb,
+                                                    stream=stream)),
+                     4.0 * wg.B * wg.H * wg.Lkv * wg.d, decode_bytes(wg), "decode"))
+
     def fp8_built():
         t = torch.zeros((1, 1, 64, 128), dtype=torch.uint8, device=dev)
         sc = torch.ones((1, 1, 1), dtype=torch.float32, device=dev)
@@ -302,6 +325,20 @@ def main():
                                "unit": "GB/s", "frac": g / PEAK_HBM_GBS,
                                "traffic": traffic_bytes("c4"),
                                "algorithmic_bytes": res["c4"]["bytes"]}}
+    decode_gqa = {}
+    for tag in ("c6", "c7"):
+        if tag in res:
+            g = res[tag]["gbs"]
+            wg = fi.WORKLOADS[int(tag[1])]
+            decode_gqa[tag] = {"workload": wg.name, "value": g, "unit": "GB/s",
+                               "ms": res[tag]["ms_mean"],
+                               "roofline": {"kernel": "fa_decode_gqa_split_kernel + "
+                                                      "fa_decode_combine_kernel",
+                                            "bound": "hbm", "achieved": g,
+                                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                            "frac": g / PEAK_HBM_GBS,
+                                            "traffic": traffic_bytes(tag),
+                                            "algorithmic_bytes": res[tag]["bytes"]}}
     prop = torch.cuda.get_device_properties(0)
     out = {
         "metric": METRIC,
@@ -317,10 +354,12 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "bf16 causal fwd B2H32N2048d128 + B1H16N16384d128 "
-                               "(value); split-KV decode B8H32Lkv65536d128 S64 (decode)",
+                               "(value); split-KV decode B8H32Lkv65536d128 S64 (decode); "
+                               "grouped decode B8 Hq64/Hkv8 and Hq32/Hkv1 Lkv65536 (decode_gqa)",
                    "only": args.only},
         "roofline": roof,
         "decode": decode,
+        "decode_gqa": decode_gqa or None,
         "workloads": res,
         "device": {"name": prop.name, "cus": prop.multi_processor_count,
                    "gcn_arch": getattr(prop, "gcnArchName", "")},

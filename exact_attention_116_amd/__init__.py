@@ -16,7 +16,7 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = ra
 FA_BF16, FA_FP32, FA_FP8_E4M3 = range(3)
 
 EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_decode_splitkv", "fa_decode_workspace_bytes",
-           "fa_decode_splitkv_ex", "fa_status_string", "fa_last_error")
+           "fa_decode_splitkv_ex", "fa_decode_splitkv_gqa", "fa_status_string", "fa_last_error")
 
 
 class FaError(RuntimeError):
@@ -58,6 +58,8 @@ def load(path: str | None = None):
     lib.fa_decode_workspace_bytes.restype = Z
     lib.fa_decode_splitkv_ex.argtypes = [P, P, P, P, P, I, I, I, I, I, F, P, Z, P]
     lib.fa_decode_splitkv_ex.restype = I
+    lib.fa_decode_splitkv_gqa.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, P, Z, P]
+    lib.fa_decode_splitkv_gqa.restype = I
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
@@ -127,3 +129,12 @@ def fa_decode_splitkv_ex(q, kcache, vcache, o, lse, B, H, Lkv, d, num_splits, sc
                                        B, H, Lkv, d, num_splits, float(scale), _ptr(workspace),
                                        int(workspace_bytes), _stream(stream)),
            "fa_decode_splitkv_ex")
+
+
+def fa_decode_splitkv_gqa(q, kcache, vcache, o, lse, B, Hq, Hkv, Lkv, d, num_splits, scale,
+                          workspace=None, workspace_bytes=0, stream=None):
+    """Grouped K/V heads: q, o bf16 [B,Hq,1,d]; caches bf16 [B,Hkv,Lkv,d]."""
+    _check(load().fa_decode_splitkv_gqa(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(o), _ptr(lse),
+                                        B, Hq, Hkv, Lkv, d, num_splits, float(scale),
+                                        _ptr(workspace), int(workspace_bytes), _stream(stream)),
+           "fa_decode_splitkv_gqa")

@@ -111,17 +111,20 @@ fa_status check_decode(const void* q, const void* kc, const void* vc, const void
   return FA_OK;
 }
 
+// Hkv = 0: plain multi-head decode (one K/V head per query head);
+// Hkv > 0: grouped heads, query head h reads K/V head h / (H / Hkv).
 fa_status run_decode(const void* q, const void* kc, const void* vc, void* o, float* lse, int B,
-                     int H, int Lkv, int d, int S, float scale, void* ws, void* stream) {
+                     int H, int Hkv, int Lkv, int d, int S, float scale, void* ws, void* stream) {
   fa::DecodeArgs a{};
   a.q = q; a.k = kc; a.v = vc; a.o = o; a.lse = lse;
   a.part_o = static_cast<float*>(ws);
   a.part_lse = static_cast<float*>(ws) + (size_t)B * H * S * d;
   a.B = B; a.H = H; a.Lkv = Lkv; a.d = d; a.num_splits = S;
+  a.Hkv = Hkv > 0 ? Hkv : H;
   a.scale_log2 = (float)((double)scale * kLog2e);
   a.stream = stream;
-  hipError_t e = fa::launch_decode(a);
-  if (e != hipSuccess) return hip_fail(e, "fa_decode_splitkv launch");
+  hipError_t e = Hkv > 0 ? fa::launch_decode_gqa(a) : fa::launch_decode(a);
+  if (e != hipSuccess) return hip_fail(e, Hkv > 0 ? "fa_decode_splitkv_gqa launch" : "fa_decode_splitkv launch");
   g_last_error.clear();
   return FA_OK;
 }
@@ -134,6 +137,36 @@ struct OwnedWorkspace {
   std::vector<size_t> bytes;
 };
 OwnedWorkspace g_ws;
+
+// The current device's library-owned workspace, at least `need` bytes.
+fa_status owned_workspace(size_t need, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_ws.mu);
+  if ((int)g_ws.ptr.size() <= dev) {
+    g_ws.ptr.resize(dev + 1, nullptr);
+    g_ws.bytes.resize(dev + 1, 0);
+  }
+  if (g_ws.bytes[dev] < need) {
+    if (g_ws.ptr[dev]) {
+      // the old buffer may still be read by queued work of an earlier call
+      e = hipDeviceSynchronize();
+      if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+      hipFree(g_ws.ptr[dev]);
+      g_ws.ptr[dev] = nullptr;
+      g_ws.bytes[dev] = 0;
+    }
+    e = hipMalloc(&g_ws.ptr[dev], need);
+    if (e != hipSuccess) {
+      g_ws.ptr[dev] = nullptr;
+      return fail(FA_ERR_WORKSPACE, "could not allocate the decode workspace");
+    }
+    g_ws.bytes[dev] = need;
+  }
+  *out = g_ws.ptr[dev];
+  return FA_OK;
+}
 
 }  // namespace
 
@@ -170,7 +203,7 @@ fa_status fa_decode_splitkv_ex(const void* q, const void* kcache, const void* vc
   if (!aligned16(workspace)) return fail(FA_ERR_WORKSPACE, "workspace must be non-NULL and 16-byte aligned");
   if (workspace_bytes < decode_ws_bytes(B, H, d, num_splits))
     return fail(FA_ERR_WORKSPACE, "workspace smaller than fa_decode_workspace_bytes()");
-  return run_decode(q, kcache, vcache, o, lse, B, H, Lkv, d, num_splits, scale, workspace, stream);
+  return run_decode(q, kcache, vcache, o, lse, B, H, 0, Lkv, d, num_splits, scale, workspace, stream);
 }
 
 fa_status fa_decode_splitkv(const void* q, const void* kcache, const void* vcache, void* o, int B,
@@ -178,36 +211,33 @@ fa_status fa_decode_splitkv(const void* q, const void* kcache, const void* vcach
   const float scale = d > 0 ? (float)(1.0 / std::sqrt((double)d)) : 0.f;
   fa_status st = check_decode(q, kcache, vcache, o, B, H, Lkv, d, num_splits, scale);
   if (st != FA_OK) return st;
-  const size_t need = decode_ws_bytes(B, H, d, num_splits);
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   void* ws = nullptr;
-  {
-    std::lock_guard<std::mutex> lock(g_ws.mu);
-    if ((int)g_ws.ptr.size() <= dev) {
-      g_ws.ptr.resize(dev + 1, nullptr);
-      g_ws.bytes.resize(dev + 1, 0);
-    }
-    if (g_ws.bytes[dev] < need) {
-      if (g_ws.ptr[dev]) {
-        // the old buffer may still be read by queued work of an earlier call
-        e = hipDeviceSynchronize();
-        if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-        hipFree(g_ws.ptr[dev]);
-        g_ws.ptr[dev] = nullptr;
-        g_ws.bytes[dev] = 0;
-      }
-      e = hipMalloc(&g_ws.ptr[dev], need);
-      if (e != hipSuccess) {
-        g_ws.ptr[dev] = nullptr;
-        return fail(FA_ERR_WORKSPACE, "could not allocate the decode workspace");
-      }
-      g_ws.bytes[dev] = need;
-    }
-    ws = g_ws.ptr[dev];
+  st = owned_workspace(decode_ws_bytes(B, H, d, num_splits), &ws);
+  if (st != FA_OK) return st;
+  return run_decode(q, kcache, vcache, o, nullptr, B, H, 0, Lkv, d, num_splits, scale, ws, nullptr);
+}
+
+fa_status fa_decode_splitkv_gqa(const void* q, const void* kcache, const void* vcache, void* o,
+                                float* lse, int B, int Hq, int Hkv, int Lkv, int d, int num_splits,
+                                float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (Hkv < 1 || Hq < 1 || Hq % Hkv != 0)
+    return fail(FA_ERR_INVALID_ARG, "Hkv must be >= 1 and divide Hq");
+  fa_status st = check_decode(q, kcache, vcache, o, B, Hq, Lkv, d, num_splits, scale);
+  if (st != FA_OK) return st;
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  const size_t need = decode_ws_bytes(B, Hq, d, num_splits);
+  void* ws = workspace;
+  if (!workspace) {
+    if (workspace_bytes != 0) return fail(FA_ERR_WORKSPACE, "workspace is NULL but workspace_bytes is not 0");
+    st = owned_workspace(need, &ws);
+    if (st != FA_OK) return st;
+  } else {
+    if (!aligned16(workspace)) return fail(FA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(FA_ERR_WORKSPACE, "workspace smaller than fa_decode_workspace_bytes()");
   }
-  return run_decode(q, kcache, vcache, o, nullptr, B, H, Lkv, d, num_splits, scale, ws, nullptr);
+  return run_decode(q, kcache, vcache, o, lse, B, Hq, Hkv, Lkv, d, num_splits, scale, ws, stream);
 }
 
 const char* fa_status_string(fa_status s) {

@@ -133,10 +133,14 @@ void fa_decode_combine_kernel(const float* __restrict__ part_o, const float* __r
   const int bh = blockIdx.x, t = threadIdx.x;
   const float* pl = part_lse + (size_t)bh * S;
   const float* po = part_o + (size_t)bh * S * D + t;
+  // (unrolled so that many independent loads are in flight: the loop is
+  // latency-bound, not bandwidth-bound)
   float M = kNegInf;
+#pragma unroll 16
   for (int s = 0; s < S; ++s) M = fmaxf(M, pl[s]);
   float W = 0.f, O = 0.f;
   if (M != kNegInf) {
+#pragma unroll 16
     for (int s = 0; s < S; ++s) {
       const float w = __builtin_amdgcn_exp2f((pl[s] - M) * kLog2e);
       W += w;
@@ -159,13 +163,23 @@ static hipError_t launch_d(const DecodeArgs& a) {
                      a.part_o, a.part_lse, a.Lkv, a.num_splits, chunk, a.scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa_decode_combine_kernel<D>), dim3(BH), dim3(D), 0, st, a.part_o, a.part_lse,
-                     (bf16*)a.o, a.lse, a.num_splits);
-  return hipGetLastError();
+  return launch_decode_combine(a);
 }
 
 hipError_t launch_decode(const DecodeArgs& a) {
   return a.d == 128 ? launch_d<128>(a) : launch_d<64>(a);
+}
+
+hipError_t launch_decode_combine(const DecodeArgs& a) {
+  const unsigned BH = (unsigned)(a.B * a.H);
+  hipStream_t st = (hipStream_t)a.stream;
+  if (a.d == 128)
+    hipLaunchKernelGGL((fa_decode_combine_kernel<128>), dim3(BH), dim3(128), 0, st, a.part_o,
+                       a.part_lse, (bf16*)a.o, a.lse, a.num_splits);
+  else
+    hipLaunchKernelGGL((fa_decode_combine_kernel<64>), dim3(BH), dim3(64), 0, st, a.part_o,
+                       a.part_lse, (bf16*)a.o, a.lse, a.num_splits);
+  return hipGetLastError();
 }
 
 }  // namespace fa

@@ -31,6 +31,24 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b,
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16).  Lane l supplies row
+// (A) / column (B) l%16 and contraction slots 8*(l/16)..+7; the result lane l
+// holds column l%16, rows 4*(l/16) + i for i = 0..3.
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Rows of 16 lanes exchange a value with the neighbouring row: returns
+// {x[l], x[l^16]} in some order.
+__device__ __forceinline__ float max_pair16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(as_u32(x), as_u32(x), false, false);
+  return fmaxf(as_f32(r[0]), as_f32(r[1]));
+}
+__device__ __forceinline__ float sum_pair16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(as_u32(x), as_u32(x), false, false);
+  return as_f32(r[0]) + as_f32(r[1]);
+}
+
 // Both halves of the wave exchange a value: returns {x[l%32], x[32 + l%32]}
 // in some order, so op(r.x, r.y) is the pairwise reduction over l and l^32.
 __device__ __forceinline__ float max_pair32(float x) {
@@ -92,6 +110,10 @@ __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
 // The same with the non-temporal hint (for data read exactly once).
 __device__ __forceinline__ u32x4 buf_load16_nt(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
+
+__device__ __forceinline__ u32x2 buf_load8_nt(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 2));
 }
 
 // Round two floats to bf16 (nearest even) and pack them (a in the low half).

@@ -33,6 +33,7 @@ struct DecodeArgs {
   float* part_o;      // [B*H, S, d] fp32
   float* part_lse;    // [B*H, S]    fp32
   int B, H, Lkv, d, num_splits;
+  int Hkv;            // key/value heads (H for plain multi-head decode)
   float scale_log2;
   void* stream;
 };
@@ -40,5 +41,8 @@ struct DecodeArgs {
 hipError_t launch_fwd_bf16(const FwdArgs& a);
 hipError_t launch_fwd_fp8(const FwdArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_decode_gqa(const DecodeArgs& a);
+// the merge of the split partials (shared by both decode paths)
+hipError_t launch_decode_combine(const DecodeArgs& a);
 
 }  // namespace fa

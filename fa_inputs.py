@@ -13,7 +13,7 @@ does:
   with one float32 scale per 64 consecutive sequence rows of each (b, h),
   ``scale = amax / 448``, ``code = round_to_nearest_even_saturating(x / scale)``.
 
-Workload shapes follow the five configurations the build is measured on (see
+Workload shapes follow the configurations the kernels are measured on (see
 ``WORKLOADS``).  Attention is defined per (batch, head) on ``[B, H, N, d]``
 row-major tensors, the layout the pages use for Q, K, V and O (FlashAttention
 note, "问题分析": ``(batch, heads, seq_len, head_dim)``).
@@ -35,7 +35,8 @@ E4M3_MAX = 448.0
 
 @dataclass(frozen=True)
 class Workload:
-    """One measured configuration.  ``kind`` is 'fwd', 'fwd_fp8' or 'decode'."""
+    """One measured configuration.  ``kind`` is 'fwd', 'fwd_fp8', 'decode' or
+    'decode_gqa' (``H`` query heads over ``Hkv`` key/value heads)."""
     wid: int
     name: str
     kind: str
@@ -47,6 +48,7 @@ class Workload:
     num_splits: int = 0
     causal: tuple = (False,)
     out_dtype: str = "bf16"
+    Hkv: int = 0    # decode_gqa only: key/value heads
     note: str = field(default="", compare=False)
 
     @property
@@ -70,6 +72,12 @@ WORKLOADS = {
     5: Workload(5, "fp8_causal_b4h16n8192d128", "fwd_fp8", 4, 16, 8192, 128,
                 causal=(True,), out_dtype="bf16",
                 note="e4m3 Q/K/V, one fp32 scale per 64 rows per head, 0.1% x20 outliers"),
+    6: Workload(6, "decode_gqa_b8hq64hkv8lkv65536d128s64", "decode_gqa", 8, 64, 1, 128,
+                Lkv=65536, num_splits=64, Hkv=8, causal=(False,), out_dtype="bf16",
+                note="grouped K/V heads (8 query heads per K/V head), 64 KiB-key cache"),
+    7: Workload(7, "decode_mqa_b8hq32hkv1lkv65536d128s64", "decode_gqa", 8, 32, 1, 128,
+                Lkv=65536, num_splits=64, Hkv=1, causal=(False,), out_dtype="bf16",
+                note="one shared K/V head for 32 query heads, 64 KiB-key cache"),
 }
 
 
@@ -227,6 +235,7 @@ def workload_inputs(w: Workload):
     fwd:     dict(q, k, v) uint16 bf16 bits [B,H,N,d]
     fwd_fp8: dict(q, k, v) uint8 e4m3 codes + (q_scale, k_scale, v_scale) float32
     decode:  dict(q [B,H,1,d], k [B,H,Lkv,d], v [B,H,Lkv,d]) uint16 bf16 bits
+    decode_gqa: the same with k, v [B,Hkv,Lkv,d]
     """
     if w.kind == "fwd":
         return {n: bf16_tensor(w.wid, t, w.B, w.H, w.N, w.d)
@@ -240,4 +249,8 @@ def workload_inputs(w: Workload):
         return {"q": bf16_tensor(w.wid, Q_ID, w.B, w.H, 1, w.d),
                 "k": bf16_tensor(w.wid, K_ID, w.B, w.H, w.Lkv, w.d),
                 "v": bf16_tensor(w.wid, V_ID, w.B, w.H, w.Lkv, w.d)}
+    if w.kind == "decode_gqa":
+        return {"q": bf16_tensor(w.wid, Q_ID, w.B, w.H, 1, w.d),
+                "k": bf16_tensor(w.wid, K_ID, w.B, w.Hkv, w.Lkv, w.d),
+                "v": bf16_tensor(w.wid, V_ID, w.B, w.Hkv, w.Lkv, w.d)}
     raise ValueError(w.kind)

@@ -1,5 +1,6 @@
 /*
- * fa.h -- exact attention (FlashAttention forward, split-KV decode) on
+ * fa.h -- exact attention (FlashAttention forward, split-KV decode with
+ * per-head or grouped K/V heads) on
  * AMD Instinct MI355X (gfx950).  C ABI: plain pointers and sizes only.
  *
  * What is computed (per batch b, head h; row-major [B, H, N, d] tensors,
@@ -25,8 +26,9 @@
  *     launched; nothing crosses the ABI as an exception.  A launch failure
  *     returns FA_ERR_HIP (fa_last_error() has the HIP text); faults inside a
  *     kernel surface at the caller's next synchronisation.
- *   - Calls that share a library-owned workspace (fa_decode_splitkv) on one
- *     device must not run concurrently on different streams.
+ *   - Calls that share a library-owned workspace (fa_decode_splitkv, and
+ *     fa_decode_splitkv_gqa with a NULL workspace) on one device must not
+ *     run concurrently on different streams.
  */
 #ifndef FA_H_
 #define FA_H_
@@ -143,6 +145,32 @@ fa_status fa_decode_splitkv_ex(const void* q, const void* kcache, const void* vc
                                float* lse, int B, int H, int Lkv, int d, int num_splits,
                                float scale, void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/*
+ * fa_decode_splitkv_gqa -- single-query split-KV decode where several query
+ * heads share one key/value head (grouped-query attention; multi-query
+ * attention when Hkv = 1: the MQA note among the related posts of the CSDN
+ * "flash attention CUDA programming, pipeline-parallel acceleration V6"
+ * page, where keys and values keep a single shared head and queries keep
+ * all of theirs).  Query head h attends over key/value head h / (Hq / Hkv).
+ *
+ * q      : bf16 [B, Hq, 1, d]          o   : bf16 [B, Hq, 1, d]
+ * kcache, vcache : bf16 [B, Hkv, Lkv, d]   lse : fp32 [B, Hq] or NULL
+ * Hkv >= 1 must divide Hq (else FA_ERR_INVALID_ARG); Hkv = Hq is plain
+ * multi-head decode.  num_splits, d, scale and the 4 GiB-per-split limit
+ * are as for fa_decode_splitkv_ex, and so is the workspace: at least
+ * fa_decode_workspace_bytes(B, Hq, d, num_splits) bytes holding partial O
+ * fp32 [B, Hq, num_splits, d] then partial LSE fp32 [B, Hq, num_splits]
+ * after the call.  workspace = NULL with workspace_bytes = 0 selects the
+ * library-owned workspace (which allocates, see fa_decode_splitkv).
+ * One workgroup streams a (batch, K/V head, split) range once for up to 16
+ * query heads of its group; groups larger than 16 read the range once per
+ * 16 heads.
+ */
+fa_status fa_decode_splitkv_gqa(const void* q, const void* kcache, const void* vcache, void* o,
+                                float* lse, int B, int Hq, int Hkv, int Lkv, int d,
+                                int num_splits, float scale, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* A static string naming the status. */
 const char* fa_status_string(fa_status s);

@@ -125,6 +125,31 @@ def test_decode_rejects(lib):
     assert lib.fa_decode_splitkv(A, A, A, A, 1, 1, 16, 32, 4) == fa.FA_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hkv=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Hkv=3), fa.FA_ERR_INVALID_ARG),      # does not divide Hq = 8
+    (dict(Hq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(vc=A + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=A + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(S=17), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(ws=None, ws_bytes=64), fa.FA_ERR_WORKSPACE),
+    (dict(ws=A + 4), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=100), fa.FA_ERR_WORKSPACE),
+    (dict(Lkv=1 << 24, S=1), fa.FA_ERR_UNSUPPORTED),
+])
+def test_decode_gqa_rejects(lib, kw, status):
+    a = dict(q=A, kc=A, vc=A, o=A, lse=None, B=1, Hq=8, Hkv=2, Lkv=16, d=128, S=4, scale=0.1,
+             ws=A, ws_bytes=1 << 20)
+    a.update(kw)
+    st = lib.fa_decode_splitkv_gqa(a["q"], a["kc"], a["vc"], a["o"], a["lse"], a["B"], a["Hq"],
+                                   a["Hkv"], a["Lkv"], a["d"], a["S"], a["scale"], a["ws"],
+                                   a["ws_bytes"], None)
+    assert st == status
+
+
 def test_binding_raises_with_status():
     with pytest.raises(fa.FaError) as e:
         fa.fa_fwd(A, A, A, A, None, 1, 1, 16, 128, 0.1, False)
