@@ -37,13 +37,25 @@ PEAK_HBM_GBS = 8000.0
 # written, so fetches are scaled by 1048576/524300 and writes by 1.  Each
 # entry is tied to the SHA-256 of its kernel source plus the shared device
 # header: once either changes, the figure no longer describes the kernel and
-# the bench reports traffic as null.
+# the bench reports traffic as null.  Split-KV decode entries add the
+# split-merge kernel's counters to the split kernel's.
 COUNTER_SCALE = {"fetch": 1048576.0 / 524300.0, "write": 1.0}
 TRAFFIC_KIB = {
-    "c3": {"src": "fa_fwd_bf16.hip", "fetch_kib": 348054.0, "write_kib": 66560.0,
-           "sha256": "38787770bb54535a289b796c2b456af1c5563f69ddd552b4388e45dcfc5b3746"},
-    "c4": {"src": "fa_decode.hip", "fetch_kib": 4194676.0 + 4172.0, "write_kib": 8706.0 + 72.0,
-           "sha256": "fb3ef4135af8a9afb791ad62ee1419918618a3d14c4d8501b91f2dcfc12190ec"},
+    "c3": {"src": ["fa_fwd_bf16.hip"], "fetch_kib": (250094.0 + 261620.0 + 248480.0) / 3,
+           "write_kib": 66560.0,
+           "sha256": "84e010ac594ba0e8e315e689168d6789394727bb8fd8429a27d17ea7624295e7"},
+    "c4": {"src": ["fa_decode.hip"],
+           "fetch_kib": (4194784.0 + 4194625.0 + 4194618.0) / 3 + 4180.0,
+           "write_kib": (8706.0 + 8707.0 + 8705.0) / 3 + 72.0,
+           "sha256": "981ba075afae4656b287e80ae205d6e3aee2a77c8eb71461d5f88c70436e85ce"},
+    "c6": {"src": ["fa_decode_gqa.hip", "fa_decode.hip"],
+           "fetch_kib": (1086608.0 + 1087127.0 + 1087528.0) / 3 + (8342.0 + 8340.0 + 8340.0) / 3,
+           "write_kib": (17410.0 + 17409.0 + 17410.0) / 3 + 144.0,
+           "sha256": "b13a0363f2e352b24df6af9f7e4f1c62d153cac0dfccbd62f457a23bc8ba756b"},
+    "c7": {"src": ["fa_decode_gqa.hip", "fa_decode.hip"],
+           "fetch_kib": (132968.0 + 133160.0 + 132813.0) / 3 + (4182.0 + 4180.0 + 4180.0) / 3,
+           "write_kib": (8704.0 + 8705.0 + 8704.0) / 3 + 72.0,
+           "sha256": "b13a0363f2e352b24df6af9f7e4f1c62d153cac0dfccbd62f457a23bc8ba756b"},
 }
 
 
@@ -54,9 +66,11 @@ def traffic_bytes(workload):
     if t is None:
         return None
     csrc = os.path.join(ROOT, "exact_attention_116_amd", "csrc")
-    with open(os.path.join(csrc, t["src"]), "rb") as f, \
-            open(os.path.join(csrc, "fa_device.hpp"), "rb") as g:
-        digest = hashlib.sha256(f.read() + g.read()).hexdigest()
+    blob = b""
+    for name in t["src"] + ["fa_device.hpp"]:
+        with open(os.path.join(csrc, name), "rb") as f:
+            blob += f.read()
+    digest = hashlib.sha256(blob).hexdigest()
     if digest != t["sha256"]:
         return None
     return 1024.0 * (t["fetch_kib"] * COUNTER_SCALE["fetch"] + t["write_kib"] * COUNTER_SCALE["write"])
