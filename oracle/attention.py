@@ -93,6 +93,59 @@ def attention_rows(q_rows, qidx, k, v, scale, causal=False):
 
 
 # ---------------------------------------------------------------------------
+# Backward: gradients of the definition (dQ, dK, dV for an upstream dO)
+# ---------------------------------------------------------------------------
+
+def _backward_rows(q, k, v, do, scale, causal, qidx):
+    """The chain rule through the definition for query rows ``qidx``.
+
+    With P = softmax_j(s_ij) and O = P V, for an upstream gradient dO:
+        dV   = P^T dO
+        dP   = dO V^T
+        dS   = P * (dP - sum_j P * dP)        (Jacobian of the row softmax)
+        dQ   = scale * dS K,   dK = scale * dS^T Q
+    Returns (dQ rows, this block's share of dK, of dV).
+    """
+    S = scale * (q @ k.T)
+    if causal:
+        j = np.arange(k.shape[0])
+        S = np.where(j[None, :] <= qidx[:, None], S, -np.inf)
+    m = S.max(axis=1)
+    E = np.exp(S - m[:, None])
+    P = E / E.sum(axis=1)[:, None]
+    dV = P.T @ do
+    dP = do @ v.T
+    dS = P * (dP - (P * dP).sum(axis=1)[:, None])
+    return scale * (dS @ k), scale * (dS.T @ q), dV
+
+
+def attention_backward(q, k, v, do, scale, causal=False, row_block=ROW_BLOCK):
+    """Gradients of sum(O * dO) with respect to q, k and v, in float64.
+
+    q, do: [..., N, d]; k, v: [..., N, d] (as many keys as queries when
+    causal, so no row is empty).  Recomputes P from q and k (the pages'
+    recomputation in place of a stored score matrix) and sums the key-side
+    gradients over blocks of query rows.  Returns (dQ, dK, dV).
+    """
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    lead = q.shape[:-2]
+    N, d = q.shape[-2:]
+    qf, kf, vf, dof = (x.reshape((-1,) + x.shape[-2:]) for x in (q, k, v, do))
+    dQ = np.empty_like(qf)
+    dK = np.zeros_like(kf)
+    dV = np.zeros_like(vf)
+    for g in range(qf.shape[0]):
+        for r0 in range(0, N, row_block):
+            idx = np.arange(r0, min(r0 + row_block, N))
+            dq, dk, dv = _backward_rows(qf[g, idx], kf[g], vf[g], dof[g, idx], scale, causal, idx)
+            dQ[g, idx] = dq
+            dK[g] += dk
+            dV[g] += dv
+    return (dQ.reshape(lead + (N, d)), dK.reshape(lead + kf.shape[-2:]),
+            dV.reshape(lead + vf.shape[-2:]))
+
+
+# ---------------------------------------------------------------------------
 # Split-KV (Flash-Decoding): partial results per key range, then the merge
 # ---------------------------------------------------------------------------
 

@@ -476,3 +476,66 @@ def test_gqa_against_torch_sdpa():
 def test_gqa_rejects_uneven_groups():
     with pytest.raises(ValueError):
         oracle.decode_attention_gqa(np.zeros((1, 3, 1, 2)), np.zeros((1, 2, 4, 2)), np.zeros((1, 2, 4, 2)), 1.0)
+
+
+# ---------------------------------------------------------------------------
+# backward: gradients of the definition
+# ---------------------------------------------------------------------------
+
+def _loss(q, k, v, do, scale, causal):
+    O, _ = oracle.attention(q, k, v, scale, causal)
+    return float(np.sum(O * do))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_finite_differences(causal):
+    """Central differences of sum(O * dO) (the forward definition only)."""
+    rng = np.random.default_rng(51 + causal)
+    N, d, scale, h = 5, 3, 0.6, 1e-5
+    q, k, v, do = (_rand(rng, N, d) for _ in range(4))
+    dQ, dK, dV = oracle.attention_backward(q, k, v, do, scale, causal)
+    for x, g in ((q, dQ), (k, dK), (v, dV)):
+        num = np.empty_like(x)
+        for idx in np.ndindex(*x.shape):
+            x0 = x[idx]
+            x[idx] = x0 + h
+            lp = _loss(q, k, v, do, scale, causal)
+            x[idx] = x0 - h
+            lm = _loss(q, k, v, do, scale, causal)
+            x[idx] = x0
+            num[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=0, atol=1e-8)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,d,scale", [(37, 16, 0.25), (130, 64, 0.125), (600, 8, 0.9)])
+def test_backward_against_torch_autograd(N, d, scale, causal):
+    rng = np.random.default_rng(N + d)
+    q, k, v, do = (_rand(rng, 2, 3, N, d) for _ in range(4))
+    dQ, dK, dV = oracle.attention_backward(q, k, v, do, scale, causal)
+    tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_() for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)
+    out.backward(torch.from_numpy(do))
+    for ours, ref in ((dQ, tq.grad), (dK, tk.grad), (dV, tv.grad)):
+        np.testing.assert_allclose(ours, ref.numpy(), rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_invariants(causal):
+    """Row-softmax gradients sum to zero over the keys, so the key gradients
+    sum to zero; each P row sums to one, so dV sums to the sum of dO; with
+    causal masking row 0 sees one key and its query gradient vanishes."""
+    rng = np.random.default_rng(61 + causal)
+    N, d = 77, 8
+    q, k, v, do = (_rand(rng, N, d) for _ in range(4))
+    dQ, dK, dV = oracle.attention_backward(q, k, v, do, 0.4, causal, row_block=16)
+    np.testing.assert_allclose(dK.sum(axis=0), 0.0, atol=1e-12)
+    np.testing.assert_allclose(dV.sum(axis=0), do.sum(axis=0), rtol=0, atol=1e-12)
+    if causal:
+        assert np.all(dQ[0] == 0.0)
+        # the last key is seen by the last query only
+        p_last = 1.0 / np.exp(oracle.attention(q, k, v, 0.4, True)[1][-1] - 0.4 * q[-1] @ k[-1])
+        np.testing.assert_allclose(dV[-1], p_last * do[-1], rtol=1e-12, atol=1e-14)
+    dQ2, dK2, dV2 = oracle.attention_backward(q, k, v, do, 0.4, causal)
+    for a, b in ((dQ, dQ2), (dK, dK2), (dV, dV2)):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
