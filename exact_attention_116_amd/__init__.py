@@ -16,7 +16,8 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = ra
 FA_BF16, FA_FP32, FA_FP8_E4M3 = range(3)
 
 EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_decode_splitkv", "fa_decode_workspace_bytes",
-           "fa_decode_splitkv_ex", "fa_decode_splitkv_gqa", "fa_status_string", "fa_last_error")
+           "fa_decode_splitkv_ex", "fa_decode_splitkv_gqa", "fa_bwd_workspace_bytes", "fa_bwd",
+           "fa_status_string", "fa_last_error")
 
 
 class FaError(RuntimeError):
@@ -60,6 +61,10 @@ def load(path: str | None = None):
     lib.fa_decode_splitkv_ex.restype = I
     lib.fa_decode_splitkv_gqa.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, P, Z, P]
     lib.fa_decode_splitkv_gqa.restype = I
+    lib.fa_bwd_workspace_bytes.argtypes = [I, I, I]
+    lib.fa_bwd_workspace_bytes.restype = Z
+    lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, Z, P]
+    lib.fa_bwd.restype = I
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
@@ -138,3 +143,15 @@ def fa_decode_splitkv_gqa(q, kcache, vcache, o, lse, B, Hq, Hkv, Lkv, d, num_spl
                                         B, Hq, Hkv, Lkv, d, num_splits, float(scale),
                                         _ptr(workspace), int(workspace_bytes), _stream(stream)),
            "fa_decode_splitkv_gqa")
+
+
+def fa_bwd_workspace_bytes(B, H, N) -> int:
+    return int(load().fa_bwd_workspace_bytes(B, H, N))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, workspace=None,
+           workspace_bytes=0, stream=None):
+    """bf16 [B,H,N,d] q, k, v, o, dout and fp32 lse [B,H,N] -> bf16 dq, dk, dv."""
+    _check(load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                         _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
+                         _ptr(workspace), int(workspace_bytes), _stream(stream)), "fa_bwd")

@@ -1,5 +1,6 @@
 // C-ABI host layer of the attention library: argument validation, the
-// library-owned decode workspace and dispatch to the HIP launchers.
+// library-owned workspace (decode partials, backward row sums) and dispatch
+// to the HIP launchers.
 // Every check runs before any HIP call, so a rejected call touches no device.
 #include <hip/hip_runtime_api.h>
 
@@ -238,6 +239,52 @@ fa_status fa_decode_splitkv_gqa(const void* q, const void* kcache, const void* v
       return fail(FA_ERR_WORKSPACE, "workspace smaller than fa_decode_workspace_bytes()");
   }
   return run_decode(q, kcache, vcache, o, lse, B, Hq, Hkv, Lkv, d, num_splits, scale, ws, stream);
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N) {
+  if (B < 1 || H < 1 || N < 1) return 0;
+  const size_t n = (size_t)B * H * (size_t)N * 4u;
+  return (n + 255u) & ~(size_t)255u;
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                 float scale, int causal, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(FA_ERR_INVALID_ARG,
+                "q, k, v, o, dout, lse, dq, dk and dv must be non-NULL and 16-byte aligned");
+  if (B < 1 || H < 1 || N < 1) return fail(FA_ERR_INVALID_ARG, "B, H and N must be >= 1");
+  if (d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1");
+  if (!good_scale(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if ((long long)B * H * ((N + 31) / 32) > 0x7FFFFFFFLL)
+    return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "backward supports d = 64 or 128");
+  if ((long long)N * d * 2 >= (1LL << 32))
+    return fail(FA_ERR_UNSUPPORTED, "one (batch, head) slice must be smaller than 4 GiB");
+  const size_t need = fa_bwd_workspace_bytes(B, H, N);
+  void* ws = workspace;
+  if (!workspace) {
+    if (workspace_bytes != 0) return fail(FA_ERR_WORKSPACE, "workspace is NULL but workspace_bytes is not 0");
+    fa_status st = owned_workspace(need, &ws);
+    if (st != FA_OK) return st;
+  } else {
+    if (!aligned16(workspace)) return fail(FA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need) return fail(FA_ERR_WORKSPACE, "workspace smaller than fa_bwd_workspace_bytes()");
+  }
+  fa::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+  a.dsum = static_cast<float*>(ws);
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.B = B; a.H = H; a.N = N; a.d = d;
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * kLog2e);
+  a.causal = causal ? 1 : 0;
+  a.stream = stream;
+  hipError_t e = fa::launch_bwd(a);
+  if (e != hipSuccess) return hip_fail(e, "fa_bwd launch");
+  g_last_error.clear();
+  return FA_OK;
 }
 
 const char* fa_status_string(fa_status s) {

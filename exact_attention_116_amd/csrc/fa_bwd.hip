@@ -1,0 +1,543 @@
+// FlashAttention backward pass (dQ, dK, dV), bf16, on gfx950 matrix cores.
+//
+// Method: the gradients of O = softmax(scale * Q K^T) V for an upstream dO,
+// with P recomputed from Q, K and the log-sum-exp the forward pass saved
+// instead of a stored score matrix (the recomputation named in the
+// FlashAttention summaries; the pages split the backward pass over thread
+// blocks in their own way in the FlashAttention-2 overview, section 3.4, and
+// keep the softmax statistics in fp32, "使用注意事项" of the Flash Attention
+// note):
+//     P  = exp(scale * Q K^T - LSE)          dV = P^T dO
+//     dP = dO V^T                            dS = P * (dP - D),  D = rowsum(dO * O)
+//     dQ = scale * dS K                      dK = scale * dS^T Q
+// (D equals rowsum(P * dP), the softmax Jacobian's correction term, because
+// O = P V.)
+//
+// Three kernels, none of which needs atomics (so the result is
+// deterministic):
+//  1. fa_bwd_pre_kernel: D per query row, fp32, from bf16 O and dO.
+//  2. fa_bwd_dkdv_kernel: key/value tiles outer, query tiles inner.  Each
+//     wave owns 32 keys; K^T and V^T stay in VGPRs as MFMA B operands.  Per
+//     32-query block it forms S = Q K^T and dP = dO V^T (one key per lane
+//     column), P and dS in-lane, then dV^T += dO^T P and dK^T += Q^T dS with
+//     P and dS fed straight in as B operands.
+//  3. fa_bwd_dq_kernel: query tiles outer, key/value tiles inner, the
+//     forward kernel's layout: Q^T and dO^T stay in VGPRs, one query per lane
+//     column, S^T = K Q^T and dP^T = V dO^T, then dQ^T += K^T dS^T.
+// Recomputing S and dP in the dQ kernel costs 40% more matrix work than
+// accumulating dQ across key tiles with fp32 atomics, which would move
+// several GB of atomic traffic per launch at these sizes.
+//
+// LDS: tiles arrive by direct global->LDS buffer loads, double-buffered.
+// Q and dO (kernel 2) and K (kernel 3) are read both row-wise (16-byte
+// fragments of one row per lane) and transposed (ds_read_b64_tr_b16), so
+// their 16-byte chunks are XOR-swizzled with a pattern that keeps both
+// reads free of bank conflicts: at 256 bytes per row, chunk c of row r sits
+// at c ^ (4*(r%4) + (r/4)%4).
+#include "fa_device.hpp"
+#include "fa_internal.h"
+
+namespace fa {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// XOR swizzle of the 16-byte chunks of LDS row r (RB bytes per row).
+template <int RB>
+__device__ __forceinline__ int bwd_swz(int r) {
+  static_assert(RB == 256 || RB == 128, "rows of 64 or 128 bf16");
+  if constexpr (RB == 256) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Direct global->LDS copy of ROWS rows of RB bytes, swizzled; NW waves share
+// the 1 KB instructions.  base_off is the byte offset of the tile's first
+// row in the buffer resource.
+template <int RB, int ROWS, int NW>
+struct TileLoader {
+  static constexpr int NI = ROWS * RB / 1024;
+  static constexpr int IPW = NI / NW;
+  static_assert(NI % NW == 0, "tile must split evenly over the waves");
+  uint32_t goff[IPW];
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int x = 0; x < IPW; ++x) {
+      const int byte = (wave * IPW + x) * 1024 + lane * 16;
+      const int r = byte / RB, p = (byte % RB) / 16;
+      goff[x] = (uint32_t)(r * RB + 16 * (p ^ bwd_swz<RB>(r)));
+    }
+  }
+  __device__ __forceinline__ void load(rsrc_t R, uint32_t base_off, uint8_t* lds, int wave) const {
+#if defined(__HIP_DEVICE_COMPILE__)  // the LDS-DMA builtin exists in the device pass only
+#pragma unroll
+    for (int x = 0; x < IPW; ++x)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          R, (__attribute__((address_space(3))) void*)(lds + (wave * IPW + x) * 1024), 16,
+          base_off + goff[x], 0, 0, 0);
+#endif
+  }
+};
+
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Per-lane LDS byte offsets for the two read patterns of a swizzled tile.
+//  row:  A operand of a 32x32x16 MFMA from row-major data: lane l reads row
+//        l%32 (+32 per block), bf16 columns 16u + 8(l/32) .. +7.
+//  tr:   A operand built from the transpose: two ds_read_b64_tr_b16 (rows
+//        +0 and +8 of a 16-row step) give lane l column 32cb + l%32 over the
+//        eight rows in the order of a 32x32 accumulator's row index.
+template <int D>
+struct TileReads {
+  static constexpr int RB = D * 2;
+  uint32_t row[D / 16];
+  uint32_t tr_lo[D / 32], tr_hi[D / 32];
+  __device__ __forceinline__ void init(int lane) {
+    const int l32 = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int u = 0; u < D / 16; ++u)
+      row[u] = (uint32_t)(l32 * RB + 16 * ((2 * u + g) ^ bwd_swz<RB>(l32)));
+    const int j16 = lane & 15, dh = (lane >> 4) & 1, q4 = j16 >> 2;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) {
+      const int c = 4 * cb + 2 * dh + ((j16 & 3) >> 1);
+      const int rl = 4 * g + q4, rh = rl + 8;
+      tr_lo[cb] = (uint32_t)(rl * RB + 16 * (c ^ bwd_swz<RB>(rl)) + 8 * (j16 & 1));
+      tr_hi[cb] = (uint32_t)(rh * RB + 16 * (c ^ bwd_swz<RB>(rh)) + 8 * (j16 & 1));
+    }
+  }
+  // row fragment u of the 32-row block starting at row r0 (a multiple of 32)
+  __device__ __forceinline__ bf16x8 rowfrag(const uint8_t* t, int r0, int u) const {
+    return *reinterpret_cast<const bf16x8*>(t + r0 * RB + row[u]);
+  }
+  // transposed fragment: rows r0 .. r0+15 (r0 a multiple of 16), columns 32cb..
+  __device__ __forceinline__ bf16x8 trfrag(const uint8_t* t, int r0, int cb) const {
+    const uint8_t* b = t + r0 * RB;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(b + tr_lo[cb]));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(b + tr_hi[cb]));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+};
+
+// ---------------------------------------------------------------------------
+// 1. D = rowsum(dO * O)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void fa_bwd_pre_kernel(const bf16* __restrict__ o, const bf16* __restrict__ dout,
+                       float* __restrict__ dsum, long long rows) {
+  constexpr int LPR = D / 8;  // lanes per row, 16 bytes each
+  const long long row = (long long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const int part = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(o + row * D + 8 * part);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(dout + row * D + 8 * part);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) acc = dot2_bf16(a[w], b[w], acc);
+  }
+  acc = group_sum<LPR>(acc);
+  if (row < rows && part == 0) dsum[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// 2. dK, dV: key tiles outer
+// ---------------------------------------------------------------------------
+template <int D, int BQ, int NW, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
+void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                        const bf16* __restrict__ v, const bf16* __restrict__ dout,
+                        const float* __restrict__ lse, const float* __restrict__ dsum,
+                        bf16* __restrict__ dk, bf16* __restrict__ dv, int BH, int N,
+                        float c /* scale*log2(e) */, float scale) {
+  constexpr int RB = D * 2;
+  constexpr int BC = NW * 32;           // keys per workgroup
+  constexpr int TILE = BQ * RB;         // bytes of one Q (or dO) tile
+  constexpr int STAGE = 2 * TILE + 2 * BQ * 4;
+  constexpr float kLog2e = 1.44269504088896340736f;
+  static_assert(BQ % 32 == 0 && BQ <= 64, "query tile of 32 or 64 rows");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int bh = blockIdx.x % BH;
+  const int kt = blockIdx.x / BH;       // heaviest (earliest keys) first under causal
+  const int k0 = kt * BC;
+  const int kw = k0 + wave * 32;        // this wave's first key
+  const int my_key = kw + l32;
+
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2u;
+  const rsrc_t Qr = make_rsrc(q + head, head_bytes);
+  const rsrc_t Or = make_rsrc(dout + head, head_bytes);
+  const rsrc_t Lr = make_rsrc(lse + (size_t)bh * N, (uint32_t)N * 4u);
+  const rsrc_t Dr = make_rsrc(dsum + (size_t)bh * N, (uint32_t)N * 4u);
+
+  // K^T and V^T of this lane's key as B operands (rows past N read as 0)
+  bf16x8 kb[D / 16], vb[D / 16];
+  {
+    const rsrc_t Kr = make_rsrc(k + head, head_bytes);
+    const rsrc_t Vr = make_rsrc(v + head, head_bytes);
+#pragma unroll
+    for (int u = 0; u < D / 16; ++u) {
+      const uint32_t off = ((uint32_t)my_key * D + 16 * u + 8 * g) * 2u;
+      kb[u] = __builtin_bit_cast(bf16x8, buf_load16(Kr, off));
+      vb[u] = __builtin_bit_cast(bf16x8, buf_load16(Vr, off));
+    }
+  }
+
+  TileLoader<RB, BQ, NW> ld;
+  ld.init(wave, lane);
+  TileReads<D> rd;
+  rd.init(lane);
+
+  const int nqt = (N + BQ - 1) / BQ;
+  const int it0 = CAUSAL ? (k0 / BQ) : 0;
+  auto load_tile = [&](int it) {
+    uint8_t* st = smem + (it & 1) * STAGE;
+    const uint32_t qoff = (uint32_t)it * BQ * RB;
+    ld.load(Qr, qoff, st, wave);
+    ld.load(Or, qoff, st + TILE, wave);
+#if defined(__HIP_DEVICE_COMPILE__)
+    // the tile's LSE and D: BQ floats each, 4 bytes per lane
+    if (wave < 2 * (BQ / 64 + (BQ % 64 != 0)) && lane < (BQ < 64 ? BQ : 64)) {
+      const int which = wave & 1, part = wave >> 1;
+      const uint32_t off = ((uint32_t)it * BQ + 64 * part + lane) * 4u;
+      uint8_t* dst = st + 2 * TILE + which * BQ * 4 + 64 * part * 4;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(which ? Dr : Lr,
+                                               (__attribute__((address_space(3))) void*)dst, 4,
+                                               off, 0, 0, 0);
+    }
+#endif
+  };
+
+  f32x16 dvt[D / 32], dkt[D / 32];
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb) {
+    dvt[cb] = f32x16{};
+    dkt[cb] = f32x16{};
+  }
+
+  if (it0 < nqt) {
+    load_tile(it0);
+    wait_vm();
+  }
+  __syncthreads();
+
+  for (int it = it0; it < nqt; ++it) {
+    const bool more = it + 1 < nqt;
+    if (more) load_tile(it + 1);
+    const uint8_t* st = smem + (it & 1) * STAGE;
+    const uint8_t* Qs = st;
+    const uint8_t* Os = st + TILE;
+    const float* Ls = reinterpret_cast<const float*>(st + 2 * TILE);
+    const float* Ds = Ls + BQ;
+
+#pragma unroll
+    for (int blk = 0; blk < BQ / 32; ++blk) {
+      const int qb0 = it * BQ + 32 * blk;    // first query of the block
+      if (CAUSAL && qb0 + 31 < kw) continue;  // every query precedes every key of this wave
+      // Four MFMA phases, each with the VALU work of the next step placed
+      // between its MFMAs so that the two overlap inside the wave:
+      //   S = Q K^T | dP = dO V^T with P | dV^T += dO^T P with dS | dK^T += Q^T dS
+      // Accumulator row i is query qb0 + 8(i/4) + 4g + i%4; this lane's key
+      // is the column.
+      const bool edge = (CAUSAL && qb0 < kw + 31) || qb0 + 32 > N;
+      f32x16 s = f32x16{};
+      {
+        constexpr int PD = 2, NF = D / 16;
+        bf16x8 f[NF];
+#pragma unroll
+        for (int i = 0; i < NF + PD; ++i) {
+          if (i < NF) f[i] = rd.rowfrag(Qs, 32 * blk, i);
+          if (i >= PD) s = mfma32x32x16(f[i - PD], kb[i - PD], s);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // P (bf16 pairs, B-operand order: slot j of k-step t is row 8t + j)
+      uint32_t pw[8];
+      auto make_p = [&](int h) {   // rows 2h, 2h+1
+        const int i = 2 * h;
+        const int qr = 32 * blk + 8 * (i >> 2) + 4 * g + (i & 3);
+        const float l0 = Ls[qr] * kLog2e, l1 = Ls[qr + 1] * kLog2e;
+        float p0 = __builtin_amdgcn_exp2f(fmaf(s[i], c, -l0));
+        float p1 = __builtin_amdgcn_exp2f(fmaf(s[i + 1], c, -l1));
+        if (edge) {
+          const int qi = it * BQ + qr;
+          if (qi >= N || (CAUSAL && my_key > qi)) p0 = 0.f;
+          if (qi + 1 >= N || (CAUSAL && my_key > qi + 1)) p1 = 0.f;
+        }
+        pw[h] = pack_bf16(p0, p1);
+      };
+      f32x16 dp = f32x16{};
+      {
+        constexpr int PD = 2, NF = D / 16;
+        bf16x8 f[NF];
+#pragma unroll
+        for (int i = 0; i < NF + PD; ++i) {
+          if (i < NF) f[i] = rd.rowfrag(Os, 32 * blk, i);
+          if (i >= PD) {
+            const int x = i - PD;
+            dp = mfma32x32x16(f[x], vb[x], dp);
+            // spread the 8 P pairs over the NF dP MFMAs
+            if constexpr (D / 16 >= 8) make_p(x);
+            else { make_p(2 * x); make_p(2 * x + 1); }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      bf16x8 pp[2];
+      pp[0] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+      pp[1] = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
+      // dS = P (dP - D), from the bf16 P the matrix cores also see
+      uint32_t sw[8];
+      auto make_ds = [&](int h) {
+        const int i = 2 * h;
+        const int qr = 32 * blk + 8 * (i >> 2) + 4 * g + (i & 3);
+        const float p0 = bf16lo(pw[h]), p1 = bf16hi(pw[h]);
+        sw[h] = pack_bf16(p0 * (dp[i] - Ds[qr]), p1 * (dp[i + 1] - Ds[qr + 1]));
+      };
+      // ---- dV^T += dO^T P (dS built between the MFMAs), then dK^T += Q^T dS ----
+      {
+        constexpr int PD = 2, NC = D / 32, NF = 2 * NC;
+        bf16x8 f[NF];
+#pragma unroll
+        for (int i = 0; i < NF + PD; ++i) {
+          if (i < NF) f[i] = rd.trfrag(Os, 32 * blk + 16 * (i / NC), i % NC);
+          if (i >= PD) {
+            const int x = i - PD;
+            dvt[x % NC] = mfma32x32x16(f[x], pp[x / NC], dvt[x % NC]);
+            if constexpr (NF >= 8) make_ds(x);
+            else { make_ds(2 * x); make_ds(2 * x + 1); }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      bf16x8 ps[2];
+      ps[0] = __builtin_bit_cast(bf16x8, u32x4{sw[0], sw[1], sw[2], sw[3]});
+      ps[1] = __builtin_bit_cast(bf16x8, u32x4{sw[4], sw[5], sw[6], sw[7]});
+      {
+        constexpr int PD = 2, NC = D / 32, NF = 2 * NC;
+        bf16x8 f[NF];
+#pragma unroll
+        for (int i = 0; i < NF + PD; ++i) {
+          if (i < NF) f[i] = rd.trfrag(Qs, 32 * blk + 16 * (i / NC), i % NC);
+          if (i >= PD) {
+            const int x = i - PD;
+            dkt[x % NC] = mfma32x32x16(f[x], ps[x / NC], dkt[x % NC]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+
+    if (more) wait_vm();
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds key my_key, features 32cb + 8(i/4) + 4g + i%4 ----
+  if (my_key < N) {
+    const size_t row = (size_t)bh * N + my_key;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int d0 = 32 * cb + 8 * ii + 4 * g;
+        *reinterpret_cast<u32x2*>(dv + row * D + d0) =
+            u32x2{pack_bf16(dvt[cb][4 * ii], dvt[cb][4 * ii + 1]),
+                  pack_bf16(dvt[cb][4 * ii + 2], dvt[cb][4 * ii + 3])};
+        *reinterpret_cast<u32x2*>(dk + row * D + d0) =
+            u32x2{pack_bf16(scale * dkt[cb][4 * ii], scale * dkt[cb][4 * ii + 1]),
+                  pack_bf16(scale * dkt[cb][4 * ii + 2], scale * dkt[cb][4 * ii + 3])};
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. dQ: query tiles outer
+// ---------------------------------------------------------------------------
+template <int D, int BC, int NW, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
+void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                      const bf16* __restrict__ v, const bf16* __restrict__ dout,
+                      const float* __restrict__ lse, const float* __restrict__ dsum,
+                      bf16* __restrict__ dq, int BH, int N, float c, float scale) {
+  constexpr int RB = D * 2;
+  constexpr int BR = NW * 32;           // queries per workgroup
+  constexpr int TILE = BC * RB;
+  constexpr int STAGE = 2 * TILE;
+  constexpr float kLog2e = 1.44269504088896340736f;
+  static_assert(BC % 32 == 0, "key tile of whole 32-key blocks");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int nqt = (N + BR - 1) / BR;
+  const int bh = blockIdx.x % BH;
+  int qt = blockIdx.x / BH;
+  if constexpr (CAUSAL) qt = nqt - 1 - qt;   // longest query tiles first
+  const int q0 = qt * BR;
+  const int qw = q0 + wave * 32;
+  const int my_q = qw + l32;
+
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2u;
+  const rsrc_t Kr = make_rsrc(k + head, head_bytes);
+  const rsrc_t Vr = make_rsrc(v + head, head_bytes);
+
+  // Q^T and dO^T of this lane's query as B operands; its LSE (base 2) and D
+  bf16x8 qb[D / 16], ob[D / 16];
+  float lse2 = 0.f, dd = 0.f;
+  {
+    const rsrc_t Qr = make_rsrc(q + head, head_bytes);
+    const rsrc_t Or = make_rsrc(dout + head, head_bytes);
+#pragma unroll
+    for (int u = 0; u < D / 16; ++u) {
+      const uint32_t off = ((uint32_t)my_q * D + 16 * u + 8 * g) * 2u;
+      qb[u] = __builtin_bit_cast(bf16x8, buf_load16(Qr, off));
+      ob[u] = __builtin_bit_cast(bf16x8, buf_load16(Or, off));
+    }
+    if (my_q < N) {
+      lse2 = lse[(size_t)bh * N + my_q] * kLog2e;
+      dd = dsum[(size_t)bh * N + my_q];
+    }
+  }
+
+  TileLoader<RB, BC, NW> ld;
+  ld.init(wave, lane);
+  TileReads<D> rd;
+  rd.init(lane);
+
+  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
+  const int ntiles = (kv_end + BC - 1) / BC;
+  auto load_tile = [&](int j) {
+    uint8_t* st = smem + (j & 1) * STAGE;
+    const uint32_t off = (uint32_t)j * BC * RB;
+    ld.load(Kr, off, st, wave);
+    ld.load(Vr, off, st + TILE, wave);
+  };
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb) acc[cb] = f32x16{};
+
+  load_tile(0);
+  wait_vm();
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    const bool more = j + 1 < ntiles;
+    if (more) load_tile(j + 1);
+    const uint8_t* Ks = smem + (j & 1) * STAGE;
+    const uint8_t* Vs = Ks + TILE;
+
+#pragma unroll
+    for (int blk = 0; blk < BC / 32; ++blk) {
+      const int kb0 = j * BC + 32 * blk;
+      if (CAUSAL && kb0 > qw + 31) continue;   // the block lies above the diagonal
+      // ---- S^T = K Q^T and dP^T = V dO^T: keys on rows, this lane's query on the column ----
+      f32x16 s = f32x16{}, dp = f32x16{};
+      {
+        constexpr int PD = 4, NF = 2 * (D / 16);
+        bf16x8 f[NF];
+#pragma unroll
+        for (int i = 0; i < NF + PD; ++i) {
+          if (i < NF) f[i] = rd.rowfrag((i & 1) ? Vs : Ks, 32 * blk, i >> 1);
+          if (i >= PD) {
+            const int x = i - PD;
+            if (x & 1) dp = mfma32x32x16(f[x], ob[x >> 1], dp);
+            else s = mfma32x32x16(f[x], qb[x >> 1], s);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // ---- dS^T (row i of the accumulator is key kb0 + 8(i/4) + 4g + i%4) ----
+      const bool edge = (CAUSAL && kb0 + 31 > qw) || kb0 + 32 > N || qw + 32 > N;
+      bf16x8 ps[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        uint32_t w[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          float dsv[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int i = 8 * t + 2 * h + e;
+            float p = __builtin_amdgcn_exp2f(fmaf(s[i], c, -lse2));
+            if (edge) {
+              const int key = kb0 + 8 * (i >> 2) + 4 * g + (i & 3);
+              if (key >= N || my_q >= N || (CAUSAL && key > my_q)) p = 0.f;
+            }
+            dsv[e] = p * (dp[i] - dd);
+          }
+          w[h] = pack_bf16(dsv[0], dsv[1]);
+        }
+        ps[t] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+      }
+      // ---- dQ^T += K^T dS^T ----
+      {
+        constexpr int PD = 4, NC = D / 32, NF = 2 * NC;
+        bf16x8 f[NF];
+#pragma unroll
+        for (int i = 0; i < NF + PD; ++i) {
+          if (i < NF) f[i] = rd.trfrag(Ks, 32 * blk + 16 * (i / NC), i % NC);
+          if (i >= PD) {
+            const int x = i - PD;
+            acc[x % NC] = mfma32x32x16(f[x], ps[x / NC], acc[x % NC]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+
+    if (more) wait_vm();
+    __syncthreads();
+  }
+
+  if (my_q < N) {
+    const size_t row = (size_t)bh * N + my_q;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int d0 = 32 * cb + 8 * ii + 4 * g;
+        *reinterpret_cast<u32x2*>(dq + row * D + d0) =
+            u32x2{pack_bf16(scale * acc[cb][4 * ii], scale * acc[cb][4 * ii + 1]),
+                  pack_bf16(scale * acc[cb][4 * ii + 2], scale * acc[cb][4 * ii + 3])};
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+static hipError_t launch_bwd_d(const BwdArgs& a) {
+  constexpr int BQ = 64, NWK = 4;    // dK/dV: 128 keys per workgroup, 64-query tiles
+  constexpr int BCQ = 64, NWQ = 8;   // dQ: 256 queries per workgroup, 64-key tiles
+  const int BH = a.B * a.H;
+  hipStream_t st = (hipStream_t)a.stream;
+  const long long rows = (long long)BH * a.N;
+  hipLaunchKernelGGL((fa_bwd_pre_kernel<D>), dim3((unsigned)((rows + (256 / (D / 8)) - 1) / (256 / (D / 8)))),
+                     dim3(256), 0, st, (const bf16*)a.o, (const bf16*)a.dout, a.dsum, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nkt = (a.N + NWK * 32 - 1) / (NWK * 32);
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BQ, NWK, CAUSAL>), dim3((unsigned)((long long)nkt * BH)),
+                     dim3(NWK * 64), 0, st, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
+                     (const bf16*)a.dout, a.lse, a.dsum, (bf16*)a.dk, (bf16*)a.dv, BH, a.N,
+                     a.scale_log2, a.scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nqt = (a.N + NWQ * 32 - 1) / (NWQ * 32);
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BCQ, NWQ, CAUSAL>), dim3((unsigned)((long long)nqt * BH)),
+                     dim3(NWQ * 64), 0, st, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
+                     (const bf16*)a.dout, a.lse, a.dsum, (bf16*)a.dq, BH, a.N, a.scale_log2,
+                     a.scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdArgs& a) {
+  if (a.d == 128) return a.causal ? launch_bwd_d<128, true>(a) : launch_bwd_d<128, false>(a);
+  return a.causal ? launch_bwd_d<64, true>(a) : launch_bwd_d<64, false>(a);
+}
+
+}  // namespace fa

@@ -38,7 +38,26 @@ struct DecodeArgs {
   void* stream;
 };
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;   // [B*H, N] natural log, from the forward pass
+  float* dsum;        // [B*H, N] workspace: rowsum(dO * O)
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, H, N, d;
+  float scale;
+  float scale_log2;
+  int causal;
+  void* stream;
+};
+
 hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_bwd(const BwdArgs& a);
 hipError_t launch_fwd_fp8(const FwdArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_decode_gqa(const DecodeArgs& a);

@@ -29,6 +29,7 @@ import numpy as np
 SEED_ROOT = 20261202
 Q_ID, K_ID, V_ID = 0, 1, 2
 OUTLIER_MASK_ID = {Q_ID: 3, K_ID: 4, V_ID: 5}
+DO_ID = 6          # the upstream gradient dO of a backward pass
 FP8_BLOCK_ROWS = 64
 E4M3_MAX = 448.0
 

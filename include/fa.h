@@ -1,6 +1,6 @@
 /*
- * fa.h -- exact attention (FlashAttention forward, split-KV decode with
- * per-head or grouped K/V heads) on
+ * fa.h -- exact attention (FlashAttention forward and backward, split-KV
+ * decode with per-head or grouped K/V heads) on
  * AMD Instinct MI355X (gfx950).  C ABI: plain pointers and sizes only.
  *
  * What is computed (per batch b, head h; row-major [B, H, N, d] tensors,
@@ -27,8 +27,8 @@
  *     returns FA_ERR_HIP (fa_last_error() has the HIP text); faults inside a
  *     kernel surface at the caller's next synchronisation.
  *   - Calls that share a library-owned workspace (fa_decode_splitkv, and
- *     fa_decode_splitkv_gqa with a NULL workspace) on one device must not
- *     run concurrently on different streams.
+ *     fa_decode_splitkv_gqa or fa_bwd with a NULL workspace) on one device
+ *     must not run concurrently on different streams.
  */
 #ifndef FA_H_
 #define FA_H_
@@ -171,6 +171,34 @@ fa_status fa_decode_splitkv_gqa(const void* q, const void* kcache, const void* v
                                 float* lse, int B, int Hq, int Hkv, int Lkv, int d,
                                 int num_splits, float scale, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/*
+ * fa_bwd -- gradients of exact attention: dQ, dK, dV for an upstream dO,
+ * with P recomputed from Q, K and the forward pass's LSE (the recomputation
+ * of the FlashAttention summaries; the FlashAttention-2 overview, section
+ * 3.4, on splitting the backward pass over thread blocks; the Flash
+ * Attention note, "使用注意事项", on fp32 softmax statistics in the backward
+ * pass).  With s_ij = scale * <q_i, k_j> (j > i masked when causal),
+ * P = exp(s - LSE), D_i = sum_c dO_ic * O_ic:
+ *     dV = P^T dO,   dS = P * (dO V^T - D),   dQ = scale * dS K,
+ *     dK = scale * dS^T Q.
+ *
+ * q, k, v, o, dout, dq, dk, dv : bf16 [B, H, N, d]   lse : fp32 [B, H, N]
+ * o and lse are the forward pass's outputs for the same q, k, v, scale and
+ * causal flag (fa_fwd / fa_fwd_ex with bf16 output).  d in {64, 128}, else
+ * FA_ERR_UNSUPPORTED; scale finite and > 0.  All pointers 16-byte aligned.
+ * The workspace holds D (fp32 [B, H, N]): at least
+ * fa_bwd_workspace_bytes(B, H, N) bytes, or NULL with workspace_bytes = 0 to
+ * use the library-owned workspace (which allocates).  dq, dk and dv are
+ * written in full (no accumulation into existing contents); the result is
+ * deterministic (no atomics).
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N);
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                 float scale, int causal, void* workspace, size_t workspace_bytes,
+                 void* stream);
 
 /* A static string naming the status. */
 const char* fa_status_string(fa_status s);
