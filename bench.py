@@ -7,6 +7,9 @@ One step = one pass of the whole hot path over resident synthetic inputs:
   * split-KV decode, B=8 H=32 Lkv=65536 d=128, 64 splits (split + merge kernels)
   * split-KV decode with grouped K/V heads, B=8 Lkv=65536 d=128, 64 splits:
     Hq=64 over Hkv=8 (GQA), and Hq=32 over one K/V head (MQA)
+  * backward (dQ, dK, dV) of the B=2 H=32 N=2048 causal and B=1 H=16 N=16384
+    causal forward passes (FLOPs counted as 2.5x the forward's: five matrix
+    products against two)
   * fp8 forward, B=4 H=16 N=8192 d=128, causal (when the library has it)
 
 ``value`` is the bf16 causal forward throughput over the N=2048 and N=16384
@@ -168,7 +171,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", default="all",
-                    help="all | c2c | c2n | c3 | c4 | c5 | c6 | c7 (profiling)")
+                    help="all | c2c | c2n | c3 | c4 | c5 | c6 | c7 | b2c | b3 (profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy per step (for HBM counter scaling)")
     args = ap.parse_args()
@@ -243,6 +246,25 @@ def main():
                                                     stream=stream)),
                      4.0 * wg.B * wg.H * wg.Lkv * wg.d, decode_bytes(wg), "decode"))
 
+    for tag, wid in (("b2c", 2), ("b3", 3)):
+        if not want(tag):
+            continue
+        wb = fi.WORKLOADS[wid]
+        log(f"generating backward B={wb.B} H={wb.H} N={wb.N} inputs")
+        qb_, kb_, vb_, dob_ = (up_bf16(fi.bf16_tensor(wb.wid, t, wb.B, wb.H, wb.N, wb.d))
+                               for t in (fi.Q_ID, fi.K_ID, fi.V_ID, fi.DO_ID))
+        ob_ = torch.empty_like(qb_)
+        lb_ = torch.empty((wb.B, wb.H, wb.N), dtype=torch.float32, device=dev)
+        fa.fa_fwd_ex(qb_, kb_, vb_, ob_, lb_, wb.B, wb.H, wb.N, wb.d, wb.scale, True, stream=stream)
+        grads = [torch.empty_like(qb_) for _ in range(3)]
+        wsb_b = fa.fa_bwd_workspace_bytes(wb.B, wb.H, wb.N)
+        wsb_ = torch.empty(wsb_b // 4, dtype=torch.float32, device=dev)
+        jobs.append((tag, (lambda w=wb, q=qb_, k=kb_, v=vb_, o=ob_, do=dob_, l=lb_, gr=grads,
+                           ws=wsb_, nb=wsb_b:
+                           fa.fa_bwd(q, k, v, o, do, l, gr[0], gr[1], gr[2], w.B, w.H, w.N, w.d,
+                                     w.scale, True, ws, nb, stream=stream)),
+                     2.5 * fwd_flops(wb, True), 8 * wb.B * wb.H * wb.N * wb.d * 2, "bwd_bf16"))
+
     def fp8_built():
         t = torch.zeros((1, 1, 64, 128), dtype=torch.uint8, device=dev)
         sc = torch.ones((1, 1, 1), dtype=torch.float32, device=dev)
@@ -312,7 +334,7 @@ def main():
         ts = np.array([evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)])
         res[name] = {"kind": kind, "ms_mean": float(ts.mean()), "ms_median": float(np.median(ts)),
                      "ms_min": float(ts.min()), "flops": flops, "bytes": nbytes}
-        if kind.startswith("fwd"):
+        if kind.startswith("fwd") or kind.startswith("bwd"):
             res[name]["tflops"] = flops / (ts.mean() * 1e-3) / 1e12
         else:
             res[name]["gbs"] = nbytes / (ts.mean() * 1e-3) / 1e9
@@ -353,6 +375,18 @@ def main():
                                             "frac": g / PEAK_HBM_GBS,
                                             "traffic": traffic_bytes(tag),
                                             "algorithmic_bytes": res[tag]["bytes"]}}
+    backward = {}
+    for tag in ("b2c", "b3"):
+        if tag in res:
+            a = res[tag]["tflops"]
+            backward[tag] = {"workload": fi.WORKLOADS[2 if tag == "b2c" else 3].name + " causal",
+                             "value": a, "unit": "TFLOPS", "ms": res[tag]["ms_mean"],
+                             "roofline": {"kernel": "fa_bwd_pre_kernel + fa_bwd_dkdv_kernel + "
+                                                    "fa_bwd_dq_kernel",
+                                          "bound": "mfma", "achieved": a,
+                                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                          "frac": a / PEAK_BF16_TFLOPS, "traffic": None,
+                                          "algorithmic_bytes": res[tag]["bytes"]}}
     prop = torch.cuda.get_device_properties(0)
     out = {
         "metric": METRIC,
@@ -369,11 +403,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": "bf16 causal fwd B2H32N2048d128 + B1H16N16384d128 "
                                "(value); split-KV decode B8H32Lkv65536d128 S64 (decode); "
-                               "grouped decode B8 Hq64/Hkv8 and Hq32/Hkv1 Lkv65536 (decode_gqa)",
+                               "grouped decode B8 Hq64/Hkv8 and Hq32/Hkv1 Lkv65536 (decode_gqa); "
+                               "causal backward of B2H32N2048d128 and B1H16N16384d128 (backward)",
                    "only": args.only},
         "roofline": roof,
         "decode": decode,
         "decode_gqa": decode_gqa or None,
+        "backward": backward or None,
         "workloads": res,
         "device": {"name": prop.name, "cus": prop.multi_processor_count,
                    "gcn_arch": getattr(prop, "gcnArchName", "")},

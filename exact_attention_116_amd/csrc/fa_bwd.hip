@@ -143,7 +143,7 @@ void fa_bwd_pre_kernel(const bf16* __restrict__ o, const bf16* __restrict__ dout
 // ---------------------------------------------------------------------------
 // 2. dK, dV: key tiles outer
 // ---------------------------------------------------------------------------
-template <int D, int BQ, int NW, bool CAUSAL>
+template <int D, int BQ, int NW, bool CAUSAL, int PD = 4>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                         const bf16* __restrict__ v, const bf16* __restrict__ dout,
@@ -155,7 +155,7 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   constexpr int TILE = BQ * RB;         // bytes of one Q (or dO) tile
   constexpr int STAGE = 2 * TILE + 2 * BQ * 4;
   constexpr float kLog2e = 1.44269504088896340736f;
-  static_assert(BQ % 32 == 0 && BQ <= 64, "query tile of 32 or 64 rows");
+  static_assert(BQ % 32 == 0 && 2 * ((BQ + 63) / 64) <= NW, "query tile of whole 32-row blocks");
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -243,9 +243,18 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       // Accumulator row i is query qb0 + 8(i/4) + 4g + i%4; this lane's key
       // is the column.
       const bool edge = (CAUSAL && qb0 < kw + 31) || qb0 + 32 > N;
+      // LSE and D of the block's rows, read now so that the LDS latency
+      // hides under the S MFMAs: group gi holds rows 8gi + 4g .. +3
+      f32x4 l4[4], d4[4];
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const int qr = 32 * blk + 8 * gi + 4 * g;
+        l4[gi] = *reinterpret_cast<const f32x4*>(Ls + qr);
+        d4[gi] = *reinterpret_cast<const f32x4*>(Ds + qr);
+      }
       f32x16 s = f32x16{};
       {
-        constexpr int PD = 2, NF = D / 16;
+        constexpr int NF = D / 16;
         bf16x8 f[NF];
 #pragma unroll
         for (int i = 0; i < NF + PD; ++i) {
@@ -259,7 +268,7 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       auto make_p = [&](int h) {   // rows 2h, 2h+1
         const int i = 2 * h;
         const int qr = 32 * blk + 8 * (i >> 2) + 4 * g + (i & 3);
-        const float l0 = Ls[qr] * kLog2e, l1 = Ls[qr + 1] * kLog2e;
+        const float l0 = l4[i >> 2][i & 3] * kLog2e, l1 = l4[i >> 2][(i & 3) + 1] * kLog2e;
         float p0 = __builtin_amdgcn_exp2f(fmaf(s[i], c, -l0));
         float p1 = __builtin_amdgcn_exp2f(fmaf(s[i + 1], c, -l1));
         if (edge) {
@@ -271,7 +280,7 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       };
       f32x16 dp = f32x16{};
       {
-        constexpr int PD = 2, NF = D / 16;
+        constexpr int NF = D / 16;
         bf16x8 f[NF];
 #pragma unroll
         for (int i = 0; i < NF + PD; ++i) {
@@ -293,13 +302,12 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       uint32_t sw[8];
       auto make_ds = [&](int h) {
         const int i = 2 * h;
-        const int qr = 32 * blk + 8 * (i >> 2) + 4 * g + (i & 3);
         const float p0 = bf16lo(pw[h]), p1 = bf16hi(pw[h]);
-        sw[h] = pack_bf16(p0 * (dp[i] - Ds[qr]), p1 * (dp[i + 1] - Ds[qr + 1]));
+        sw[h] = pack_bf16(p0 * (dp[i] - d4[i >> 2][i & 3]), p1 * (dp[i + 1] - d4[i >> 2][(i & 3) + 1]));
       };
       // ---- dV^T += dO^T P (dS built between the MFMAs), then dK^T += Q^T dS ----
       {
-        constexpr int PD = 2, NC = D / 32, NF = 2 * NC;
+        constexpr int NC = D / 32, NF = 2 * NC;
         bf16x8 f[NF];
 #pragma unroll
         for (int i = 0; i < NF + PD; ++i) {
@@ -317,7 +325,7 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       ps[0] = __builtin_bit_cast(bf16x8, u32x4{sw[0], sw[1], sw[2], sw[3]});
       ps[1] = __builtin_bit_cast(bf16x8, u32x4{sw[4], sw[5], sw[6], sw[7]});
       {
-        constexpr int PD = 2, NC = D / 32, NF = 2 * NC;
+        constexpr int NC = D / 32, NF = 2 * NC;
         bf16x8 f[NF];
 #pragma unroll
         for (int i = 0; i < NF + PD; ++i) {
@@ -511,8 +519,12 @@ void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_d(const BwdArgs& a) {
-  constexpr int BQ = 64, NWK = 4;    // dK/dV: 128 keys per workgroup, 64-query tiles
-  constexpr int BCQ = 64, NWQ = 8;   // dQ: 256 queries per workgroup, 64-key tiles
+  // dK/dV: 128 keys per workgroup (one wave per SIMD: the resident K^T, V^T
+  // and the two accumulators need ~330 registers), 64-query tiles.
+  // dQ: 256 queries per workgroup, 128-key tiles.  Both measured against
+  // 32/128-query and 32/64-key tiles in one process.
+  constexpr int BQ = 64, NWK = 4;
+  constexpr int BCQ = 128, NWQ = 8;
   const int BH = a.B * a.H;
   hipStream_t st = (hipStream_t)a.stream;
   const long long rows = (long long)BH * a.N;
