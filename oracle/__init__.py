@@ -13,7 +13,9 @@ attention   the plain definition O = softmax(scale*Q*K^T)*V with its
             log-sum-exp, in float64, score matrix materialised, two passes
             (max, then exp/sum); the split-KV partials over key ranges and
             their log-sum-exp-weighted merge; single-query decode with
-            grouped key/value heads; the gradients dQ, dK, dV of the
+            grouped key/value heads; packed batches of sequences with
+            unequal query and key lengths (causal masking aligned at the
+            sequence end); the gradients dQ, dK, dV of the
             definition (the chain rule through the row softmax, P recomputed
             from Q and K); the elementwise error bound of
             an fp8-P kernel; attention with only P rounded to E4M3FN (the
@@ -27,5 +29,5 @@ from .codecs import decode_bf16, decode_e4m3fn, dequant_fp8_rows, round_to_e4m3f
 from .attention import (  # noqa: F401
     attention, attention_rows, split_bounds, split_partials, merge_partials,
     decode_attention, decode_attention_gqa, fp8_p_error_bound, fp8_p_attention,
-    attention_backward,
+    attention_backward, attention_varlen,
 )

@@ -93,6 +93,48 @@ def attention_rows(q_rows, qidx, k, v, scale, causal=False):
 
 
 # ---------------------------------------------------------------------------
+# Ragged batches: packed sequences of unequal lengths
+# ---------------------------------------------------------------------------
+
+def attention_varlen(q, k, v, cu_q, cu_k, scale, causal=False):
+    """Exact attention over a batch of packed sequences of unequal lengths.
+
+    q: [total_q, H, d], k, v: [total_k, H, d] (tokens of sequence b at rows
+    cu_q[b]:cu_q[b+1] and cu_k[b]:cu_k[b+1]).  Causal masking is aligned at
+    the end of the sequences: with Lq queries and Lk keys, query i sees key j
+    iff j <= i + (Lk - Lq), so the queries are the last Lq positions of a
+    length-Lk sequence (a chunk of a prefill against the keys already
+    cached); for Lq == Lk this is the usual j <= i.  A query that sees no key
+    gets O = 0 and LSE = -inf.  Returns (O [total_q, H, d], LSE [H, total_q]).
+    """
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    total_q, H, d = q.shape
+    O = np.zeros((total_q, H, v.shape[-1]))
+    L = np.full((H, total_q), -np.inf)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        Lq, Lk = q1 - q0, k1 - k0
+        if Lq == 0 or Lk == 0:
+            continue
+        for h in range(H):
+            S = scale * (q[q0:q1, h] @ k[k0:k1, h].T)               # [Lq, Lk]
+            if causal:
+                i = np.arange(Lq)[:, None]
+                j = np.arange(Lk)[None, :]
+                S = np.where(j <= i + (Lk - Lq), S, -np.inf)
+            m = S.max(axis=1)
+            seen = np.isfinite(m)
+            ms = np.where(seen, m, 0.0)
+            E = np.exp(S - ms[:, None])
+            l = E.sum(axis=1)
+            with np.errstate(invalid="ignore", divide="ignore"):
+                P = np.where(seen[:, None], E / l[:, None], 0.0)
+            O[q0:q1, h] = P @ v[k0:k1, h]
+            L[h, q0:q1] = np.where(seen, ms + np.log(np.where(seen, l, 1.0)), -np.inf)
+    return O, L
+
+
+# ---------------------------------------------------------------------------
 # Backward: gradients of the definition (dQ, dK, dV for an upstream dO)
 # ---------------------------------------------------------------------------
 

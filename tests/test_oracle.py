@@ -539,3 +539,71 @@ def test_backward_invariants(causal):
     dQ2, dK2, dV2 = oracle.attention_backward(q, k, v, do, 0.4, causal)
     for a, b in ((dQ, dQ2), (dK, dK2), (dV, dV2)):
         np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# ragged batches (packed sequences, unequal query/key lengths)
+# ---------------------------------------------------------------------------
+
+def _pack(rng, lens, H, d):
+    return _rand(rng, int(sum(lens)), H, d), np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_equal_lengths_is_dense_attention(causal):
+    rng = np.random.default_rng(71 + causal)
+    lens, H, d = [5, 17, 1, 40], 3, 8
+    q, cu = _pack(rng, lens, H, d)
+    k, _ = _pack(rng, lens, H, d)
+    v, _ = _pack(rng, lens, H, d)
+    O, L = oracle.attention_varlen(q, k, v, cu, cu, 0.3, causal)
+    for b, n in enumerate(lens):
+        sl = slice(cu[b], cu[b + 1])
+        Od, Ld = oracle.attention(q[sl].transpose(1, 0, 2), k[sl].transpose(1, 0, 2),
+                                  v[sl].transpose(1, 0, 2), 0.3, causal)
+        np.testing.assert_allclose(O[sl], Od.transpose(1, 0, 2), rtol=0, atol=1e-13)
+        np.testing.assert_allclose(L[:, sl], Ld, rtol=0, atol=1e-13)
+
+
+def test_varlen_chunked_prefill_is_tail_of_full_causal():
+    """Lq new queries against Lk >= Lq keys, end-aligned: exactly the last Lq
+    rows of causal attention over the whole length-Lk sequence."""
+    rng = np.random.default_rng(73)
+    H, d = 2, 16
+    for Lk, Lq in [(50, 7), (64, 64), (33, 1), (100, 37)]:
+        qf, kf, vf = (_rand(rng, H, Lk, d) for _ in range(3))
+        Ofull, Lfull = oracle.attention(qf, kf, vf, 0.25, True)
+        q = qf[:, Lk - Lq:].transpose(1, 0, 2)
+        O, L = oracle.attention_varlen(q, kf.transpose(1, 0, 2), vf.transpose(1, 0, 2),
+                                       [0, Lq], [0, Lk], 0.25, True)
+        np.testing.assert_allclose(O, Ofull[:, Lk - Lq:].transpose(1, 0, 2), rtol=0, atol=1e-13)
+        np.testing.assert_allclose(L, Lfull[:, Lk - Lq:], rtol=0, atol=1e-13)
+
+
+def test_varlen_against_torch_masked_sdpa():
+    """More queries than keys (leading rows see nothing) and more keys than
+    queries, against torch float64 SDPA with the explicit boolean mask."""
+    rng = np.random.default_rng(79)
+    H, d = 2, 8
+    lq, lk = [9, 3, 12], [4, 10, 12]
+    q, cuq = _pack(rng, lq, H, d)
+    k, cuk = _pack(rng, lk, H, d)
+    v, _ = _pack(rng, lk, H, d)
+    O, L = oracle.attention_varlen(q, k, v, cuq, cuk, 0.5, True)
+    for b in range(3):
+        Lq, Lk = lq[b], lk[b]
+        qs = torch.from_numpy(q[cuq[b]:cuq[b + 1]].transpose(1, 0, 2).copy())
+        ks = torch.from_numpy(k[cuk[b]:cuk[b + 1]].transpose(1, 0, 2).copy())
+        vs = torch.from_numpy(v[cuk[b]:cuk[b + 1]].transpose(1, 0, 2).copy())
+        mask = torch.from_numpy(np.arange(Lk)[None, :] <= np.arange(Lq)[:, None] + (Lk - Lq))
+        seen = mask.any(dim=1).numpy()
+        ref = torch.nn.functional.scaled_dot_product_attention(qs, ks, vs, attn_mask=mask, scale=0.5)
+        got = O[cuq[b]:cuq[b + 1]].transpose(1, 0, 2)
+        np.testing.assert_allclose(got[:, seen], ref.numpy()[:, seen], rtol=0, atol=1e-12)
+        assert np.all(got[:, ~seen] == 0.0)
+        assert np.all(np.isneginf(L[:, cuq[b]:cuq[b + 1]][:, ~seen]))
+        scores = 0.5 * (qs @ ks.transpose(1, 2))
+        lse_ref = torch.logsumexp(scores.masked_fill(~mask, float("-inf")), dim=-1).numpy()
+        np.testing.assert_allclose(L[:, cuq[b]:cuq[b + 1]][:, seen], lse_ref[:, seen], rtol=0, atol=1e-12)
+    # sequence 0 (9 queries, 4 keys): its first 5 queries see no key
+    assert np.all(np.isneginf(L[:, :5])) and np.all(np.isfinite(L[:, 5:9]))
