@@ -7,6 +7,9 @@ One step = one pass of the whole hot path over resident synthetic inputs:
   * split-KV decode, B=8 H=32 Lkv=65536 d=128, 64 splits (split + merge kernels)
   * split-KV decode with grouped K/V heads, B=8 Lkv=65536 d=128, 64 splits:
     Hq=64 over Hkv=8 (GQA), and Hq=32 over one K/V head (MQA)
+  * ragged chunked prefill: 8 packed sequences of unequal lengths, H=32,
+    d=128, each a chunk of new queries against its cached keys, causal
+    aligned at the sequence end (FLOPs: 4*d per visible query-key pair)
   * backward (dQ, dK, dV) of the B=2 H=32 N=2048 causal and B=1 H=16 N=16384
     causal forward passes (FLOPs counted as 2.5x the forward's: five matrix
     products against two)
@@ -171,7 +174,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", default="all",
-                    help="all | c2c | c2n | c3 | c4 | c5 | c6 | c7 | b2c | b3 (profiling)")
+                    help="all | c2c | c2n | c3 | c4 | c5 | c6 | c7 | c8 | b2c | b3 (profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy per step (for HBM counter scaling)")
     args = ap.parse_args()
@@ -245,6 +248,34 @@ def main():
                                                     w.num_splits, w.scale, ws, nb,
                                                     stream=stream)),
                      4.0 * wg.B * wg.H * wg.Lkv * wg.d, decode_bytes(wg), "decode"))
+
+    if want("c8"):
+        wv = fi.VARLEN_PREFILL
+        log(f"generating ragged prefill inputs ({len(wv['lq'])} sequences)")
+        Hv, dv_ = wv["H"], wv["d"]
+
+        def packed(tensor, lens):
+            out = np.empty((int(sum(lens)), Hv, dv_), dtype=np.uint16)
+            r = 0
+            for b, n in enumerate(lens):
+                for h in range(Hv):
+                    out[r:r + n, h] = fi.bf16_slice(wv["wid"], tensor, b, h, n, dv_)
+                r += n
+            return up_bf16(out)
+        q8 = packed(fi.Q_ID, wv["lq"])
+        k8, v8 = packed(fi.K_ID, wv["lk"]), packed(fi.V_ID, wv["lk"])
+        o8 = torch.empty_like(q8)
+        l8 = torch.empty((Hv, q8.shape[0]), dtype=torch.float32, device=dev)
+        cq8 = torch.tensor(np.concatenate([[0], np.cumsum(wv["lq"])]), dtype=torch.int32, device=dev)
+        ck8 = torch.tensor(np.concatenate([[0], np.cumsum(wv["lk"])]), dtype=torch.int32, device=dev)
+        # visible pairs: query i of a chunk sees min(Lk, i + 1 + Lk - Lq) keys
+        pairs = sum(sum(min(lk, i + 1 + lk - lq) for i in range(lq))
+                    for lq, lk in zip(wv["lq"], wv["lk"]))
+        jobs.append(("c8", lambda: fa.fa_fwd_varlen(
+            q8, k8, v8, o8, l8, cq8, ck8, len(wv["lq"]), Hv, max(wv["lq"]), max(wv["lk"]),
+            q8.shape[0], k8.shape[0], dv_, dv_ ** -0.5, True, stream=stream),
+            4.0 * dv_ * Hv * pairs, (2 * q8.numel() + k8.numel() + v8.numel()) * 2 + l8.numel() * 4,
+            "fwd_bf16"))
 
     for tag, wid in (("b2c", 2), ("b3", 3)):
         if not want(tag):
@@ -375,6 +406,15 @@ def main():
                                             "frac": g / PEAK_HBM_GBS,
                                             "traffic": traffic_bytes(tag),
                                             "algorithmic_bytes": res[tag]["bytes"]}}
+    varlen = None
+    if "c8" in res:
+        a = res["c8"]["tflops"]
+        varlen = {"workload": fi.VARLEN_PREFILL["name"], "value": a, "unit": "TFLOPS",
+                  "ms": res["c8"]["ms_mean"],
+                  "roofline": {"kernel": "fa_fwd_bf16_kernel (packed)", "bound": "mfma",
+                               "achieved": a, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                               "frac": a / PEAK_BF16_TFLOPS, "traffic": None,
+                               "algorithmic_bytes": res["c8"]["bytes"]}}
     backward = {}
     for tag in ("b2c", "b3"):
         if tag in res:
@@ -404,11 +444,13 @@ def main():
         "config": {"workload": "bf16 causal fwd B2H32N2048d128 + B1H16N16384d128 "
                                "(value); split-KV decode B8H32Lkv65536d128 S64 (decode); "
                                "grouped decode B8 Hq64/Hkv8 and Hq32/Hkv1 Lkv65536 (decode_gqa); "
-                               "causal backward of B2H32N2048d128 and B1H16N16384d128 (backward)",
+                               "causal backward of B2H32N2048d128 and B1H16N16384d128 (backward); "
+                               "ragged chunked prefill of 8 packed sequences H32d128 (varlen_prefill)",
                    "only": args.only},
         "roofline": roof,
         "decode": decode,
         "decode_gqa": decode_gqa or None,
+        "varlen_prefill": varlen,
         "backward": backward or None,
         "workloads": res,
         "device": {"name": prop.name, "cus": prop.multi_processor_count,

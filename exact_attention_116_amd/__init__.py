@@ -16,7 +16,8 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = ra
 FA_BF16, FA_FP32, FA_FP8_E4M3 = range(3)
 
 EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_decode_splitkv", "fa_decode_workspace_bytes",
-           "fa_decode_splitkv_ex", "fa_decode_splitkv_gqa", "fa_bwd_workspace_bytes", "fa_bwd",
+           "fa_decode_splitkv_ex", "fa_decode_splitkv_gqa", "fa_fwd_varlen",
+           "fa_bwd_workspace_bytes", "fa_bwd",
            "fa_status_string", "fa_last_error")
 
 
@@ -61,6 +62,8 @@ def load(path: str | None = None):
     lib.fa_decode_splitkv_ex.restype = I
     lib.fa_decode_splitkv_gqa.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, P, Z, P]
     lib.fa_decode_splitkv_gqa.restype = I
+    lib.fa_fwd_varlen.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
+    lib.fa_fwd_varlen.restype = I
     lib.fa_bwd_workspace_bytes.argtypes = [I, I, I]
     lib.fa_bwd_workspace_bytes.restype = Z
     lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, Z, P]
@@ -155,3 +158,12 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, workspa
     _check(load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                          _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
                          _ptr(workspace), int(workspace_bytes), _stream(stream)), "fa_bwd")
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, max_seqlen_q, max_seqlen_k,
+                  total_q, total_k, d, scale, causal, stream=None):
+    """Packed bf16 q [total_q,H,d], k, v [total_k,H,d] -> o, fp32 lse [H,total_q]."""
+    _check(load().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, H, max_seqlen_q,
+                                max_seqlen_k, total_q, total_k, d, float(scale),
+                                int(bool(causal)), _stream(stream)), "fa_fwd_varlen")

@@ -83,6 +83,9 @@ fa_status run_fwd(const fa_fwd_params* p) {
   a.causal = p->causal != 0;
   a.out_f32 = p->out_dtype == FA_FP32;
   a.stream = p->stream;
+  a.cu_q = nullptr;
+  a.cu_k = nullptr;
+  a.Nk = p->N;
   hipError_t e = (p->in_dtype == FA_FP8_E4M3) ? fa::launch_fwd_fp8(a) : fa::launch_fwd_bf16(a);
   if (e == hipErrorNotSupported) return fail(FA_ERR_UNSUPPORTED, "no kernel for this request");
   if (e != hipSuccess) return hip_fail(e, "fa_fwd launch");
@@ -239,6 +242,46 @@ fa_status fa_decode_splitkv_gqa(const void* q, const void* kcache, const void* v
       return fail(FA_ERR_WORKSPACE, "workspace smaller than fa_decode_workspace_bytes()");
   }
   return run_decode(q, kcache, vcache, o, lse, B, Hq, Hkv, Lkv, d, num_splits, scale, ws, stream);
+}
+
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H,
+                        int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int d,
+                        float scale, int causal, void* stream) {
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return fail(FA_ERR_INVALID_ARG, "q, k, v, o and lse must be non-NULL and 16-byte aligned");
+  if (!cu_seqlens_q || !cu_seqlens_k ||
+      ((reinterpret_cast<uintptr_t>(cu_seqlens_q) | reinterpret_cast<uintptr_t>(cu_seqlens_k)) & 3u))
+    return fail(FA_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_k must be non-NULL and 4-byte aligned");
+  if (B < 1 || H < 1) return fail(FA_ERR_INVALID_ARG, "B and H must be >= 1");
+  if (max_seqlen_q < 1 || max_seqlen_k < 1 || total_q < 1 || total_k < 1)
+    return fail(FA_ERR_INVALID_ARG, "max_seqlen_q, max_seqlen_k, total_q and total_k must be >= 1");
+  if (d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1");
+  if (!good_scale(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "varlen path supports d = 64 or 128");
+  if ((long long)B * H * ((max_seqlen_q + 255) / 256) > 0x7FFFFFFFLL)
+    return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
+  // one sequence of one head is addressed with 32-bit byte offsets over its rows
+  const long long row_bytes = (long long)H * d * 2;
+  if ((long long)max_seqlen_q * row_bytes >= (1LL << 32) || (long long)max_seqlen_k * row_bytes >= (1LL << 32))
+    return fail(FA_ERR_UNSUPPORTED, "one sequence must span under 4 GiB of rows");
+  fa::FwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.H = H; a.N = max_seqlen_q; a.d = d;
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * kLog2e);
+  a.causal = causal ? 1 : 0;
+  a.out_f32 = 0;
+  a.stream = stream;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.Nk = max_seqlen_k;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  hipError_t e = fa::launch_fwd_bf16(a);
+  if (e != hipSuccess) return hip_fail(e, "fa_fwd_varlen launch");
+  g_last_error.clear();
+  return FA_OK;
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N) {

@@ -40,6 +40,11 @@
 //  * Causal: key tiles entirely above the diagonal are never loaded; within
 //    a workgroup, a wave whose 32 queries all precede a tile skips its math;
 //    masking is applied only on tiles that straddle the diagonal or N.
+//  * Packed batches of unequal lengths use the same kernel with runtime
+//    strides: each workgroup finds its sequence's query and key rows from
+//    the cumulative lengths, and causal masking is aligned at the sequence
+//    end (query i sees key j iff j <= i + Lk - Lq).  A query that sees no
+//    key gets O = 0 and LSE = -inf.
 //    Query tiles are launched heaviest first.  Consecutive workgroups take
 //    different heads, so with B*H a multiple of 8 every query tile of a
 //    head lands on the same XCD (dispatch is round-robin over the 8 XCDs)
@@ -60,12 +65,21 @@ struct FwdCfg {
   static_assert(BC % 32 == 0 && D % 32 == 0, "tile shapes");
 };
 
+// Where one (sequence, head) lives.  Dense: [B, H, N, d] with N keys per
+// query row set.  Packed: [total, H, d] rows with cumulative lengths.
+struct FwdLayout {
+  const int* cu_q;     // null for dense
+  const int* cu_k;
+  int H, N, Nk, total_q, total_k;   // N, Nk: longest query / key sequence
+};
+
 template <int D, int BC, int NW, bool CAUSAL, bool OUT_F32>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                         const bf16* __restrict__ v, void* __restrict__ o,
-                        float* __restrict__ lse, int BH, int N, float c /* scale*log2(e) */) {
+                        float* __restrict__ lse, int BH, FwdLayout lay,
+                        float c /* scale*log2(e) */) {
   using C = FwdCfg<D, BC, NW>;
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * (C::KTILE + C::VTILE)];
 
@@ -73,29 +87,47 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
 
-  const int nqt = (N + C::BR - 1) / C::BR;
   const int bh = blockIdx.x % BH;
   int qt = blockIdx.x / BH;
+  // this (sequence, head): first rows, lengths, row stride and LSE offset
+  int Lq = lay.N, Lk = lay.N, rs = D;
+  size_t qbase, kbase, lbase;
+  if (lay.cu_q) {
+    const int b = bh / lay.H, h = bh % lay.H;
+    const int sq = min(max(lay.cu_q[b], 0), lay.total_q);
+    const int sk = min(max(lay.cu_k[b], 0), lay.total_k);
+    Lq = min(max(min(lay.cu_q[b + 1], lay.total_q) - sq, 0), lay.N);
+    Lk = min(max(min(lay.cu_k[b + 1], lay.total_k) - sk, 0), lay.Nk);
+    rs = lay.H * D;
+    qbase = (size_t)sq * rs + (size_t)h * D;
+    kbase = (size_t)sk * rs + (size_t)h * D;
+    lbase = (size_t)h * lay.total_q + sq;
+  } else {
+    qbase = kbase = (size_t)bh * (size_t)lay.N * D;
+    lbase = (size_t)bh * lay.N;
+  }
+  const int nqt = (Lq + C::BR - 1) / C::BR;
   if constexpr (CAUSAL) qt = nqt - 1 - qt;  // longest query tiles first
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const bf16* Qh = q + head;
-  const bf16* Kh = k + head;
-  const bf16* Vh = v + head;
+  if (qt < 0 || qt >= nqt) return;          // past this sequence's queries (whole workgroup)
+  const int off = CAUSAL ? Lk - Lq : 0;     // causal: query i sees keys j <= i + off
+  const bf16* Qh = q + qbase;
+  const bf16* Kh = k + kbase;
+  const bf16* Vh = v + kbase;
+  const uint32_t RG = (uint32_t)rs * 2u;    // bytes from one row to the next in HBM
 
   const int q0 = qt * C::BR;
   const int qw = q0 + wave * 32;   // first query of this wave
   const int my_q = qw + l32;       // the query this lane's columns belong to
 
-  const uint32_t head_bytes = (uint32_t)N * D * 2u;
-  const rsrc_t Qr = make_rsrc(Qh, head_bytes);
-  const rsrc_t Kr = make_rsrc(Kh, head_bytes);
-  const rsrc_t Vr = make_rsrc(Vh, head_bytes);
+  const rsrc_t Qr = make_rsrc(Qh, (uint32_t)Lq * RG);
+  const rsrc_t Kr = make_rsrc(Kh, (uint32_t)Lk * RG);
+  const rsrc_t Vr = make_rsrc(Vh, (uint32_t)Lk * RG);
   bf16x8 qb[D / 16];
 #pragma unroll
   for (int u = 0; u < D / 16; ++u)
-    qb[u] = __builtin_bit_cast(bf16x8, buf_load16(Qr, ((uint32_t)my_q * D + 16 * u + 8 * g) * 2u));
+    qb[u] = __builtin_bit_cast(bf16x8, buf_load16(Qr, (uint32_t)my_q * RG + (16u * u + 8u * g) * 2u));
 
-  const int kv_end = CAUSAL ? min(N, q0 + C::BR) : N;
+  const int kv_end = CAUSAL ? max(0, min(Lk, q0 + C::BR + off)) : Lk;
   const int ntiles = (kv_end + BC - 1) / BC;
 
   // Direct global -> LDS loads.  One wave instruction fills 1 KB of LDS
@@ -114,11 +146,11 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const int blk = wave * IPW + x;
     const int byte = blk * 1024 + lane * 16;
     const int r = byte / RB, p = (byte % RB) / 16;
-    gk[x] = (uint32_t)(r * RB + 16 * (p ^ (r % NCH)));
-    gv[x] = (uint32_t)(r * RB + 16 * (p ^ (2 * (r & 3))));
+    gk[x] = (uint32_t)r * RG + (uint32_t)(16 * (p ^ (r % NCH)));
+    gv[x] = (uint32_t)r * RG + (uint32_t)(16 * (p ^ (2 * (r & 3))));
   }
   auto load_tile = [&](int j) {
-    const uint32_t tile = (uint32_t)j * BC * RB;
+    const uint32_t tile = (uint32_t)j * BC * RG;
     uint8_t* Kd = reinterpret_cast<uint8_t*>(smem + (j & 1) * (C::KTILE + C::VTILE));
     uint8_t* Vd = Kd + C::KTILE * 2;
 #if defined(__HIP_DEVICE_COMPILE__)  // the LDS-DMA builtin exists in the device pass only
@@ -165,7 +197,7 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     if (more) load_tile(j + 1);
 
     const int kb = j * BC;
-    const bool active = !CAUSAL || kb <= qw + 31;
+    const bool active = !CAUSAL || kb <= qw + 31 + off;
     if (active) {
       const bf16* Ks = smem + buf * (C::KTILE + C::VTILE);
       const bf16* Vs = Ks + C::KTILE;
@@ -197,14 +229,14 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       }
 
       // ---- mask keys past the diagonal or past N (edge tiles only) ----
-      const bool edge = (CAUSAL && kb + BC - 1 > qw) || kb + BC > N;
+      const bool edge = (CAUSAL && kb + BC - 1 > qw + off) || kb + BC > Lk;
       if (edge) {
 #pragma unroll
         for (int b = 0; b < BC / 32; ++b)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = kb + 32 * b + 8 * (i >> 2) + 4 * g + (i & 3);
-            const bool dead = key >= N || (CAUSAL && key > my_q);
+            const bool dead = key >= Lk || (CAUSAL && key > my_q + off);
             s[b][i] = dead ? kNegInf : s[b][i];
           }
       }
@@ -275,11 +307,12 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     __syncthreads();
   }
 
-  // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2 ----
+  // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2 (0 and -inf for a
+  // query that saw no key) ----
   l = sum_pair32(l);
-  const float inv = 1.f / l;
-  if (my_q < N) {
-    const size_t row = (size_t)bh * N + my_q;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (my_q < Lq) {
+    const size_t orow = qbase + (size_t)my_q * rs;
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
@@ -288,24 +321,25 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         const float o0 = acc[cb][4 * ii] * inv, o1 = acc[cb][4 * ii + 1] * inv;
         const float o2 = acc[cb][4 * ii + 2] * inv, o3 = acc[cb][4 * ii + 3] * inv;
         if constexpr (OUT_F32) {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(o) + row * D + d0) = f32x4{o0, o1, o2, o3};
+          *reinterpret_cast<f32x4*>(static_cast<float*>(o) + orow + d0) = f32x4{o0, o1, o2, o3};
         } else {
-          *reinterpret_cast<u32x2*>(static_cast<bf16*>(o) + row * D + d0) =
+          *reinterpret_cast<u32x2*>(static_cast<bf16*>(o) + orow + d0) =
               u32x2{pack_bf16(o0, o1), pack_bf16(o2, o3)};
         }
       }
-    if (g == 0) lse[row] = (m + __builtin_amdgcn_logf(l)) * kLn2;
+    if (g == 0) lse[lbase + my_q] = l > 0.f ? (m + __builtin_amdgcn_logf(l)) * kLn2 : kNegInf;
   }
 }
 
 template <int D, int BC, int NW, bool CAUSAL, bool OUT_F32>
 static hipError_t launch(const FwdArgs& a) {
   using C = FwdCfg<D, BC, NW>;
-  const int nqt = (a.N + C::BR - 1) / C::BR;
+  const int nqt = (a.N + C::BR - 1) / C::BR;   // of the longest sequence
   const long long blocks = (long long)nqt * a.B * a.H;
+  const FwdLayout lay{a.cu_q, a.cu_k, a.H, a.N, a.Nk, a.total_q, a.total_k};
   hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, BC, NW, CAUSAL, OUT_F32>), dim3((unsigned)blocks),
                      dim3(C::NT), 0, (hipStream_t)a.stream, (const bf16*)a.q, (const bf16*)a.k,
-                     (const bf16*)a.v, a.o, a.lse, a.B * a.H, a.N, a.scale_log2);
+                     (const bf16*)a.v, a.o, a.lse, a.B * a.H, lay, a.scale_log2);
   return hipGetLastError();
 }
 

@@ -20,6 +20,14 @@ struct FwdArgs {
   float scale;        // softmax scale
   float scale_log2;   // scale * log2(e)
   int causal;
+  // packed sequences of unequal lengths (bf16 path): q, k, v, o are
+  // [total, H, d] token-major, lse is [H, total_q]; sequence b occupies rows
+  // cu_q[b]..cu_q[b+1] (queries) and cu_k[b]..cu_k[b+1] (keys).  N is the
+  // largest query length, Nk the largest key length.  Null cu_q: dense
+  // [B, H, N, d] tensors with as many keys as queries.
+  const int* cu_q;
+  const int* cu_k;
+  int Nk, total_q, total_k;
   int out_f32;
   void* stream;
 };

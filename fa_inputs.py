@@ -82,6 +82,17 @@ WORKLOADS = {
 }
 
 
+# A ragged chunked-prefill batch: 8 sequences, each a chunk of new queries
+# (lq) against its cached keys plus itself (lk = cached + lq), H=32, d=128,
+# causal masking aligned at the sequence end.  Lengths mix short and long
+# chunks and short and long caches.
+VARLEN_PREFILL = {
+    "wid": 8, "name": "chunked_prefill_ragged_b8h32d128", "H": 32, "d": 128,
+    "lq": [2048, 1024, 512, 256, 1536, 768, 128, 1800],
+    "lk": [2048, 2048, 4608, 6256, 2048, 2816, 8192, 2048],
+}
+
+
 def _workers() -> int:
     try:
         n = len(os.sched_getaffinity(0))

@@ -173,6 +173,34 @@ fa_status fa_decode_splitkv_gqa(const void* q, const void* kcache, const void* v
                                 size_t workspace_bytes, void* stream);
 
 /*
+ * fa_fwd_varlen -- the bf16 forward pass over a batch of packed sequences of
+ * unequal lengths (the power-of-two length rule of the Flash Attention
+ * note, "使用注意事项", does not apply: any lengths work).  Sequence b has
+ * Lq = cu_seqlens_q[b+1] - cu_seqlens_q[b] queries and Lk =
+ * cu_seqlens_k[b+1] - cu_seqlens_k[b] keys; Lq and Lk may differ.
+ *
+ * q, o   : bf16 [total_q, H, d] (token-major; sequence b at rows cu_seqlens_q[b]..)
+ * k, v   : bf16 [total_k, H, d]
+ * lse    : fp32 [H, total_q]
+ * cu_seqlens_q, cu_seqlens_k : int32 DEVICE arrays of B+1 non-decreasing
+ *          offsets starting at 0, ending at total_q / total_k.
+ * max_seqlen_q, max_seqlen_k : bounds on Lq and Lk (they size the launch;
+ *          longer sequences are cut to them).  The kernel clamps every
+ *          offset to [0, total], so malformed offsets give wrong values but
+ *          no access outside the tensors.
+ * causal : masking aligned at the end of each sequence -- query i sees key
+ *          j iff j <= i + (Lk - Lq): the queries are the last Lq positions
+ *          of a length-Lk sequence, as for a prefill chunk against cached
+ *          keys.  A query that sees no key (Lq > Lk) gets O = 0, LSE = -inf.
+ * d in {64, 128}; bf16 output; one sequence's rows of one tensor must span
+ * under 4 GiB (max_seqlen * H * d * 2 < 2^32), else FA_ERR_UNSUPPORTED.
+ */
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H,
+                        int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int d,
+                        float scale, int causal, void* stream);
+
+/*
  * fa_bwd -- gradients of exact attention: dQ, dK, dV for an upstream dO,
  * with P recomputed from Q, K and the forward pass's LSE (the recomputation
  * of the FlashAttention summaries; the FlashAttention-2 overview, section

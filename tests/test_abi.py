@@ -150,6 +150,28 @@ def test_decode_gqa_rejects(lib, kw, status):
     assert st == status
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=A + 4), fa.FA_ERR_INVALID_ARG),
+    (dict(cuq=None), fa.FA_ERR_INVALID_ARG),
+    (dict(cuk=A + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(mq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(tk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(mk=1 << 20, H=32), fa.FA_ERR_UNSUPPORTED),   # 8 GiB of key rows
+])
+def test_fwd_varlen_rejects(lib, kw, status):
+    a = dict(q=A, k=A, v=A, o=A, lse=A, cuq=A, cuk=A, B=2, H=4, mq=64, mk=64, tq=100, tk=100,
+             d=128, scale=0.1, causal=1)
+    a.update(kw)
+    st = lib.fa_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cuq"], a["cuk"], a["B"],
+                           a["H"], a["mq"], a["mk"], a["tq"], a["tk"], a["d"], a["scale"],
+                           a["causal"], None)
+    assert st == status
+
+
 def test_binding_raises_with_status():
     with pytest.raises(fa.FaError) as e:
         fa.fa_fwd(A, A, A, A, None, 1, 1, 16, 128, 0.1, False)
