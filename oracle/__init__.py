@@ -20,6 +20,9 @@ attention   the plain definition O = softmax(scale*Q*K^T)*V with its
             from Q and K); the elementwise error bound of
             an fp8-P kernel; attention with only P rounded to E4M3FN (the
             yardstick for an fp8 kernel's mean error).
+rotation    incoherent processing for fp8: the random-sign Walsh-Hadamard
+            rotation of Q and K along the head dimension, and 64-row block
+            quantisation to E4M3FN.
 
 Every function is pinned by ``tests/test_oracle*.py`` against brute force,
 a library routine (torch's float64 scaled-dot-product attention on the CPU)
@@ -31,3 +34,4 @@ from .attention import (  # noqa: F401
     decode_attention, decode_attention_gqa, fp8_p_error_bound, fp8_p_attention,
     attention_backward, attention_varlen,
 )
+from .rotation import hadamard_matrix, incoherent_rotation, quantize_e4m3_blocks  # noqa: F401

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import fa_inputs as fi
 import oracle
 from oracle import attention, attention_rows, merge_partials, split_partials
 
@@ -607,3 +608,57 @@ def test_varlen_against_torch_masked_sdpa():
         np.testing.assert_allclose(L[:, cuq[b]:cuq[b + 1]][:, seen], lse_ref[:, seen], rtol=0, atol=1e-12)
     # sequence 0 (9 queries, 4 keys): its first 5 queries see no key
     assert np.all(np.isneginf(L[:, :5])) and np.all(np.isfinite(L[:, 5:9]))
+
+
+# ---------------------------------------------------------------------------
+# incoherent processing (random-sign Hadamard rotation) and block quantisation
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [1, 2, 8, 64, 128])
+def test_hadamard_matches_scipy_and_is_orthogonal(n):
+    from scipy.linalg import hadamard
+    H = oracle.hadamard_matrix(n)
+    np.testing.assert_array_equal(H, hadamard(n))
+    np.testing.assert_array_equal(H @ H.T, n * np.eye(n))
+
+
+def test_rotation_preserves_scores_and_spreads_outliers():
+    rng = np.random.default_rng(81)
+    d = 128
+    s = rng.choice([-1.0, 1.0], size=d)
+    q, k = _rand(rng, 40, d), _rand(rng, 30, d)
+    qr, kr = oracle.incoherent_rotation(q, s), oracle.incoherent_rotation(k, s)
+    np.testing.assert_allclose(qr @ kr.T, q @ k.T, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(np.linalg.norm(qr, axis=1), np.linalg.norm(q, axis=1), rtol=1e-14)
+    # a one-hot row becomes a row of +-1/sqrt(d)
+    e = np.zeros(d)
+    e[37] = 5.0
+    np.testing.assert_allclose(np.abs(oracle.incoherent_rotation(e, s)), 5.0 / np.sqrt(d), rtol=1e-15)
+    # the attention of rotated Q, K equals that of Q, K
+    v = _rand(rng, 30, 16)
+    O1, L1 = oracle.attention(qr, kr, v, 0.2, False)
+    O2, L2 = oracle.attention(q, k, v, 0.2, False)
+    np.testing.assert_allclose(O1, O2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L1, L2, rtol=0, atol=1e-12)
+
+
+def test_block_quantisation_matches_the_generator_quantiser():
+    """Two independent E4M3FN quantisers (grid search here, bit arithmetic in
+    the input generator) agree except where x/scale is a rounding tie."""
+    rng = np.random.default_rng(83)
+    x = rng.standard_normal((200, 128)).astype(np.float32)
+    x[rng.random(x.shape) < 1e-3] *= 20
+    vals, scales, ratio = oracle.quantize_e4m3_blocks(x)
+    codes, gscales = fi.quantize_e4m3_rows(x)
+    np.testing.assert_allclose(scales, gscales, rtol=1e-7)
+    ours = oracle.round_to_e4m3fn(ratio)          # grid values, before scaling back
+    theirs = oracle.decode_e4m3fn(codes)
+    assert np.mean(ours == theirs) > 0.9999
+    # any disagreement is one grid step at a near-tie of x / scale
+    diff = ours != theirs
+    grid_step = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ours[diff]), 2 ** -6))) - 3)
+    assert np.all(np.abs(ours[diff] - theirs[diff]) <= grid_step * 1.0000001)
+    assert np.all(np.abs(np.abs(ratio[diff]) - (np.abs(ours[diff]) + np.abs(theirs[diff])) / 2)
+                  <= 1e-6 * np.abs(ratio[diff]))
+    assert np.max(np.abs(ratio)) <= 448.0 and np.all(scales > 0)
+    np.testing.assert_allclose(vals, ours * scales[np.arange(200) // 64][:, None], rtol=1e-15)
