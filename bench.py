@@ -7,6 +7,9 @@ One step = one pass of the whole hot path over resident synthetic inputs:
   * split-KV decode, B=8 H=32 Lkv=65536 d=128, 64 splits (split + merge kernels)
   * split-KV decode with grouped K/V heads, B=8 Lkv=65536 d=128, 64 splits:
     Hq=64 over Hkv=8 (GQA), and Hq=32 over one K/V head (MQA)
+  * bf16 -> block-scaled fp8 quantisation of the fp8 workload's Q and K
+    (with the incoherent Hadamard rotation) and V, the input pass of the fp8
+    forward from bf16 activations (HBM-bound: 2 bytes read, 1 written)
   * ragged chunked prefill: 8 packed sequences of unequal lengths, H=32,
     d=128, each a chunk of new queries against its cached keys, causal
     aligned at the sequence end (FLOPs: 4*d per visible query-key pair)
@@ -174,7 +177,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", default="all",
-                    help="all | c2c | c2n | c3 | c4 | c5 | c6 | c7 | c8 | b2c | b3 (profiling)")
+                    help="all | c2c | c2n | c3 | c4 | c5 | q5 | c6 | c7 | c8 | b2c | b3 (profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy per step (for HBM counter scaling)")
     args = ap.parse_args()
@@ -248,6 +251,22 @@ def main():
                                                     w.num_splits, w.scale, ws, nb,
                                                     stream=stream)),
                      4.0 * wg.B * wg.H * wg.Lkv * wg.d, decode_bytes(wg), "decode"))
+
+    if want("q5"):
+        log("generating bf16 inputs of the fp8 workload for the quantisation pass")
+        xq = [up_bf16(fi.outlier_bf16_tensor(w5.wid, t, w5.B, w5.H, w5.N, w5.d))
+              for t in (fi.Q_ID, fi.K_ID, fi.V_ID)]
+        sg5 = torch.from_numpy(fi.rotation_signs(w5.wid, w5.d)).to(dev)
+        cq5 = [torch.empty(x.shape, dtype=torch.uint8, device=dev) for x in xq]
+        sq5 = [torch.empty((w5.B, w5.H, (w5.N + 63) // 64), dtype=torch.float32, device=dev)
+               for _ in xq]
+
+        def runq5():
+            for i, x in enumerate(xq):
+                fa.fa_fp8_quantize(x, sg5 if i < 2 else None, cq5[i], sq5[i], w5.B, w5.H, w5.N,
+                                   w5.d, stream=stream)
+        nq = xq[0].numel()
+        jobs.append(("q5", runq5, 0.0, 3 * nq * 3 + 3 * sq5[0].numel() * 4, "quant"))
 
     if want("c8"):
         wv = fi.VARLEN_PREFILL
@@ -415,6 +434,15 @@ def main():
                                "achieved": a, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                "frac": a / PEAK_BF16_TFLOPS, "traffic": None,
                                "algorithmic_bytes": res["c8"]["bytes"]}}
+    quant = None
+    if "q5" in res:
+        g = res["q5"]["gbs"]
+        quant = {"workload": w5.name + " bf16 -> fp8, Q and K rotated", "value": g, "unit": "GB/s",
+                 "ms": res["q5"]["ms_mean"],
+                 "roofline": {"kernel": "fa_fp8_quant_kernel (x3)", "bound": "hbm",
+                              "achieved": g, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                              "frac": g / PEAK_HBM_GBS, "traffic": None,
+                              "algorithmic_bytes": res["q5"]["bytes"]}}
     backward = {}
     for tag in ("b2c", "b3"):
         if tag in res:
@@ -445,12 +473,14 @@ def main():
                                "(value); split-KV decode B8H32Lkv65536d128 S64 (decode); "
                                "grouped decode B8 Hq64/Hkv8 and Hq32/Hkv1 Lkv65536 (decode_gqa); "
                                "causal backward of B2H32N2048d128 and B1H16N16384d128 (backward); "
-                               "ragged chunked prefill of 8 packed sequences H32d128 (varlen_prefill)",
+                               "ragged chunked prefill of 8 packed sequences H32d128 (varlen_prefill); "
+                               "bf16->fp8 quantisation of the fp8 workload (fp8_quantize)",
                    "only": args.only},
         "roofline": roof,
         "decode": decode,
         "decode_gqa": decode_gqa or None,
         "varlen_prefill": varlen,
+        "fp8_quantize": quant,
         "backward": backward or None,
         "workloads": res,
         "device": {"name": prop.name, "cus": prop.multi_processor_count,

@@ -16,7 +16,7 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = ra
 FA_BF16, FA_FP32, FA_FP8_E4M3 = range(3)
 
 EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_decode_splitkv", "fa_decode_workspace_bytes",
-           "fa_decode_splitkv_ex", "fa_decode_splitkv_gqa", "fa_fwd_varlen",
+           "fa_decode_splitkv_ex", "fa_decode_splitkv_gqa", "fa_fwd_varlen", "fa_fp8_quantize",
            "fa_bwd_workspace_bytes", "fa_bwd",
            "fa_status_string", "fa_last_error")
 
@@ -64,6 +64,8 @@ def load(path: str | None = None):
     lib.fa_decode_splitkv_gqa.restype = I
     lib.fa_fwd_varlen.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
     lib.fa_fwd_varlen.restype = I
+    lib.fa_fp8_quantize.argtypes = [P, P, P, P, I, I, I, I, P]
+    lib.fa_fp8_quantize.restype = I
     lib.fa_bwd_workspace_bytes.argtypes = [I, I, I]
     lib.fa_bwd_workspace_bytes.restype = Z
     lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, Z, P]
@@ -167,3 +169,9 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, max_seqlen_
                                 _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, H, max_seqlen_q,
                                 max_seqlen_k, total_q, total_k, d, float(scale),
                                 int(bool(causal)), _stream(stream)), "fa_fwd_varlen")
+
+
+def fa_fp8_quantize(x, signs, codes, scales, B, H, N, d, stream=None):
+    """bf16 [B,H,N,d] -> E4M3FN codes + fp32 [B,H,ceil(N/64)] scales; signs [d] rotates."""
+    _check(load().fa_fp8_quantize(_ptr(x), _ptr(signs), _ptr(codes), _ptr(scales), B, H, N, d,
+                                  _stream(stream)), "fa_fp8_quantize")

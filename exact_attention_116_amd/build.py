@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_fp8.hip", "fa_decode.hip", "fa_decode_gqa.hip", "fa_bwd.hip",
+SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_fp8.hip", "fa_decode.hip", "fa_decode_gqa.hip", "fa_bwd.hip", "fa_fp8_quant.hip",
            "fa_api.cpp"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -284,6 +284,28 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
   return FA_OK;
 }
 
+fa_status fa_fp8_quantize(const void* x, const float* signs, void* codes, float* scales, int B,
+                          int H, int N, int d, void* stream) {
+  if (!aligned16(x) || !aligned16(codes) || !scales || (reinterpret_cast<uintptr_t>(scales) & 3u))
+    return fail(FA_ERR_INVALID_ARG,
+                "x and codes must be non-NULL and 16-byte aligned, scales non-NULL and 4-byte aligned");
+  if (signs && (reinterpret_cast<uintptr_t>(signs) & 3u))
+    return fail(FA_ERR_INVALID_ARG, "signs must be 4-byte aligned");
+  if (B < 1 || H < 1 || N < 1) return fail(FA_ERR_INVALID_ARG, "B, H and N must be >= 1");
+  if (d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "quantisation supports d = 64 or 128");
+  if ((long long)B * H * ((N + 63) / 64) > 0x7FFFFFFFLL)
+    return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
+  fa::QuantArgs a{};
+  a.x = x; a.signs = signs; a.codes = codes; a.scales = scales;
+  a.B = B; a.H = H; a.N = N; a.d = d;
+  a.stream = stream;
+  hipError_t e = fa::launch_fp8_quant(a);
+  if (e != hipSuccess) return hip_fail(e, "fa_fp8_quantize launch");
+  g_last_error.clear();
+  return FA_OK;
+}
+
 size_t fa_bwd_workspace_bytes(int B, int H, int N) {
   if (B < 1 || H < 1 || N < 1) return 0;
   const size_t n = (size_t)B * H * (size_t)N * 4u;

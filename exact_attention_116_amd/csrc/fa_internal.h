@@ -64,7 +64,17 @@ struct BwdArgs {
   void* stream;
 };
 
+struct QuantArgs {
+  const void* x;        // bf16 [B, H, N, d]
+  const float* signs;   // [d] +-1, or null for no rotation
+  void* codes;          // u8 [B, H, N, d]
+  float* scales;        // [B, H, ceil(N/64)]
+  int B, H, N, d;
+  void* stream;
+};
+
 hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_fp8_quant(const QuantArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
 hipError_t launch_fwd_fp8(const FwdArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);

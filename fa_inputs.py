@@ -30,6 +30,7 @@ SEED_ROOT = 20261202
 Q_ID, K_ID, V_ID = 0, 1, 2
 OUTLIER_MASK_ID = {Q_ID: 3, K_ID: 4, V_ID: 5}
 DO_ID = 6          # the upstream gradient dO of a backward pass
+SIGNS_ID = 7       # the random signs of an incoherent rotation
 FP8_BLOCK_ROWS = 64
 E4M3_MAX = 448.0
 
@@ -222,6 +223,31 @@ def fp8_slice(wid: int, tensor_id: int, b: int, h: int, rows: int, d: int,
         m = stream(wid, OUTLIER_MASK_ID[tensor_id], b, h).random(size=(rows, d)) < outlier_p
         x[m] *= np.float32(outlier_mult)
     return quantize_e4m3_rows(x)
+
+
+def outlier_bf16_tensor(wid: int, tensor_id: int, B: int, H: int, rows: int, d: int,
+                        outlier_p: float = 1e-3, outlier_mult: float = 20.0) -> np.ndarray:
+    """uint16 bf16 bits [B, H, rows, d]: the fp8 workload's values (N(0,1) with
+    x20 outliers at rate 1e-3, same streams) rounded to bf16 instead of being
+    quantised, as the input of an on-GPU quantisation."""
+    out = np.empty((B, H, rows, d), dtype=np.uint16)
+
+    def fill(bh):
+        b, h = divmod(bh, H)
+        x = normals(wid, tensor_id, b, h, rows, d)
+        if outlier_p > 0:
+            m = stream(wid, OUTLIER_MASK_ID[tensor_id], b, h).random(size=(rows, d)) < outlier_p
+            x[m] *= np.float32(outlier_mult)
+        out[b, h] = f32_to_bf16_bits(x)
+
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(fill, range(B * H)))
+    return out
+
+
+def rotation_signs(wid: int, d: int) -> np.ndarray:
+    """float32 [d] of +-1: the random signs of an incoherent rotation."""
+    return stream(wid, SIGNS_ID, 0, 0).choice(np.array([-1.0, 1.0], np.float32), size=d)
 
 
 def fp8_tensor(wid: int, tensor_id: int, B: int, H: int, rows: int, d: int,

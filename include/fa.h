@@ -201,6 +201,26 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
                         float scale, int causal, void* stream);
 
 /*
+ * fa_fp8_quantize -- bf16 -> the fp8 forward pass's input format, with the
+ * optional incoherent processing of the FlashAttention-3 snippets (named
+ * there beside block quantisation as the way FA-3 lowers fp8 error; read
+ * here as a random orthogonal rotation of the head dimension).
+ *
+ * x      : bf16 [B, H, N, d]              codes  : uint8 E4M3FN [B, H, N, d]
+ * signs  : fp32 [d] of +1/-1, or NULL     scales : fp32 [B, H, ceil(N/64)]
+ * With signs, every row is first replaced by x diag(signs) H_d / sqrt(d)
+ * (H_d the Sylvester-ordered Walsh-Hadamard matrix).  Quantise Q and K with
+ * the same signs (Q K^T is unchanged) and V with NULL.  Then, per 64-row
+ * block, scale = max|x| / 448 (1 for an all-zero block) and each code is
+ * the fp32 ratio x * (448 / max|x|) -- within about an ulp of x / scale --
+ * rounded to nearest, ties to even (so a value within an ulp of a rounding
+ * midpoint of x / scale may take either neighbour).  d in {64, 128}, else
+ * FA_ERR_UNSUPPORTED.  x and codes 16-byte aligned.
+ */
+fa_status fa_fp8_quantize(const void* x, const float* signs, void* codes, float* scales, int B,
+                          int H, int N, int d, void* stream);
+
+/*
  * fa_bwd -- gradients of exact attention: dQ, dK, dV for an upstream dO,
  * with P recomputed from Q, K and the forward pass's LSE (the recomputation
  * of the FlashAttention summaries; the FlashAttention-2 overview, section

@@ -172,6 +172,22 @@ def test_fwd_varlen_rejects(lib, kw, status):
     assert st == status
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), fa.FA_ERR_INVALID_ARG),
+    (dict(codes=A + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(scales=None), fa.FA_ERR_INVALID_ARG),
+    (dict(signs=A + 1), fa.FA_ERR_INVALID_ARG),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+])
+def test_fp8_quantize_rejects(lib, kw, status):
+    a = dict(x=A, signs=None, codes=A, scales=A, B=1, H=2, N=100, d=128)
+    a.update(kw)
+    st = lib.fa_fp8_quantize(a["x"], a["signs"], a["codes"], a["scales"], a["B"], a["H"], a["N"],
+                             a["d"], None)
+    assert st == status
+
+
 def test_binding_raises_with_status():
     with pytest.raises(fa.FaError) as e:
         fa.fa_fwd(A, A, A, A, None, 1, 1, 16, 128, 0.1, False)
