@@ -52,7 +52,7 @@ COUNTER_SCALE = {"fetch": 1048576.0 / 524300.0, "write": 1.0}
 TRAFFIC_KIB = {
     "c3": {"src": ["fa_fwd_bf16.hip"], "fetch_kib": (257391.0 + 247438.0 + 264977.0) / 3,
            "write_kib": 66560.0,
-           "sha256": "0929486a48b42dd87110bb7e828b3236de235834de3460feb7beb8d926598389"},
+           "sha256": "fbd8adce8d194650079a59af12a8c67212e0222eefade8fc9ab65323d8d2266d"},
     "c4": {"src": ["fa_decode.hip"],
            "fetch_kib": (4194784.0 + 4194625.0 + 4194618.0) / 3 + 4180.0,
            "write_kib": (8706.0 + 8707.0 + 8705.0) / 3 + 72.0,

@@ -157,7 +157,7 @@ fa_status owned_workspace(size_t need, void** out) {
       // the old buffer may still be read by queued work of an earlier call
       e = hipDeviceSynchronize();
       if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-      hipFree(g_ws.ptr[dev]);
+      (void)hipFree(g_ws.ptr[dev]);  // the buffer is dropped either way
       g_ws.ptr[dev] = nullptr;
       g_ws.bytes[dev] = 0;
     }

@@ -170,8 +170,8 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
   const rsrc_t Qr = make_rsrc(q + head, head_bytes);
   const rsrc_t Or = make_rsrc(dout + head, head_bytes);
-  const rsrc_t Lr = make_rsrc(lse + (size_t)bh * N, (uint32_t)N * 4u);
-  const rsrc_t Dr = make_rsrc(dsum + (size_t)bh * N, (uint32_t)N * 4u);
+  [[maybe_unused]] const rsrc_t Lr = make_rsrc(lse + (size_t)bh * N, (uint32_t)N * 4u);
+  [[maybe_unused]] const rsrc_t Dr = make_rsrc(dsum + (size_t)bh * N, (uint32_t)N * 4u);
 
   // K^T and V^T of this lane's key as B operands (rows past N read as 0)
   bf16x8 kb[D / 16], vb[D / 16];

@@ -37,7 +37,7 @@ void fa_fp8_quant_kernel(const bf16* __restrict__ x, const float* __restrict__ s
   constexpr int RB = D * 2;             // bytes per bf16 row
   constexpr int NCH = RB / 16;          // 16-byte chunks per row
   constexpr int ROWS = 64;              // one scale block
-  constexpr int NI = ROWS * RB / 1024;  // 1 KB direct-load instructions per block
+  [[maybe_unused]] constexpr int NI = ROWS * RB / 1024;  // 1 KB direct-load instructions per block
   static_assert(D == 64 || D == 128, "d of 64 or 128");
   __shared__ __attribute__((aligned(16))) uint8_t tile[ROWS * RB];
   __shared__ float sg[D];
@@ -47,7 +47,7 @@ void fa_fp8_quant_kernel(const bf16* __restrict__ x, const float* __restrict__ s
   const int r0 = rt * ROWS;
   const size_t head = (size_t)bh * (size_t)N * D;
   const int rows_here = min(ROWS, N - r0);
-  const rsrc_t Xr = make_rsrc(x + head + (size_t)r0 * D, (uint32_t)rows_here * RB);
+  [[maybe_unused]] const rsrc_t Xr = make_rsrc(x + head + (size_t)r0 * D, (uint32_t)rows_here * RB);
 
 #if defined(__HIP_DEVICE_COMPILE__)  // the LDS-DMA builtin exists in the device pass only
 #pragma unroll

@@ -120,8 +120,8 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int my_q = qw + l32;       // the query this lane's columns belong to
 
   const rsrc_t Qr = make_rsrc(Qh, (uint32_t)Lq * RG);
-  const rsrc_t Kr = make_rsrc(Kh, (uint32_t)Lk * RG);
-  const rsrc_t Vr = make_rsrc(Vh, (uint32_t)Lk * RG);
+  [[maybe_unused]] const rsrc_t Kr = make_rsrc(Kh, (uint32_t)Lk * RG);
+  [[maybe_unused]] const rsrc_t Vr = make_rsrc(Vh, (uint32_t)Lk * RG);
   bf16x8 qb[D / 16];
 #pragma unroll
   for (int u = 0; u < D / 16; ++u)
@@ -150,9 +150,9 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     gv[x] = (uint32_t)r * RG + (uint32_t)(16 * (p ^ (2 * (r & 3))));
   }
   auto load_tile = [&](int j) {
-    const uint32_t tile = (uint32_t)j * BC * RG;
+    [[maybe_unused]] const uint32_t tile = (uint32_t)j * BC * RG;
     uint8_t* Kd = reinterpret_cast<uint8_t*>(smem + (j & 1) * (C::KTILE + C::VTILE));
-    uint8_t* Vd = Kd + C::KTILE * 2;
+    [[maybe_unused]] uint8_t* Vd = Kd + C::KTILE * 2;
 #if defined(__HIP_DEVICE_COMPILE__)  // the LDS-DMA builtin exists in the device pass only
 #pragma unroll
     for (int x = 0; x < IPW; ++x) {
