@@ -13,7 +13,8 @@ attention   the plain definition O = softmax(scale*Q*K^T)*V with its
             log-sum-exp, in float64, score matrix materialised, two passes
             (max, then exp/sum); the split-KV partials over key ranges and
             their log-sum-exp-weighted merge; single-query decode with
-            grouped key/value heads; packed batches of sequences with
+            grouped key/value heads, also over a padded cache with a length
+            per sequence; packed batches of sequences with
             unequal query and key lengths (causal masking aligned at the
             sequence end); the gradients dQ, dK, dV of the
             definition (the chain rule through the row softmax, P recomputed
@@ -32,6 +33,6 @@ from .codecs import decode_bf16, decode_e4m3fn, dequant_fp8_rows, round_to_e4m3f
 from .attention import (  # noqa: F401
     attention, attention_rows, split_bounds, split_partials, merge_partials,
     decode_attention, decode_attention_gqa, fp8_p_error_bound, fp8_p_attention,
-    attention_backward, attention_varlen,
+    attention_backward, attention_varlen, decode_attention_ragged,
 )
 from .rotation import hadamard_matrix, incoherent_rotation, quantize_e4m3_blocks  # noqa: F401

@@ -273,6 +273,27 @@ def decode_attention_gqa(q, k, v, scale):
     return attention(q, k[..., kv_of, :, :], v[..., kv_of, :, :], scale, causal=False)
 
 
+def decode_attention_ragged(q, k, v, seqlens, scale):
+    """Single-query decode over a padded cache with a length per sequence:
+    sequence b attends over the first seqlens[b] cached keys only (grouped
+    heads as in ``decode_attention_gqa``).  A sequence with no cached key
+    gets O = 0 and LSE = -inf.
+
+    q: [B, Hq, 1, d]; k, v: [B, Hkv, Lcap, d]; seqlens: [B], 0 <= seqlens[b] <= Lcap.
+    Returns (O [B, Hq, 1, d], LSE [B, Hq, 1]).
+    """
+    q = np.asarray(q, np.float64)
+    B, Hq = q.shape[:2]
+    O = np.zeros(q.shape[:3] + (np.shape(v)[-1],))
+    L = np.full((B, Hq, 1), -np.inf)
+    for b in range(B):
+        n = int(seqlens[b])
+        if n > 0:
+            O[b], L[b] = decode_attention_gqa(q[b], np.asarray(k[b])[:, :n], np.asarray(v[b])[:, :n],
+                                              scale)
+    return O, L
+
+
 # ---------------------------------------------------------------------------
 # fp8: the elementwise bound on an fp8-P kernel's error
 # ---------------------------------------------------------------------------

@@ -662,3 +662,28 @@ def test_block_quantisation_matches_the_generator_quantiser():
                   <= 1e-6 * np.abs(ratio[diff]))
     assert np.max(np.abs(ratio)) <= 448.0 and np.all(scales > 0)
     np.testing.assert_allclose(vals, ours * scales[np.arange(200) // 64][:, None], rtol=1e-15)
+
+
+def test_ragged_decode_is_varlen_attention_with_one_query():
+    """Per-sequence cache lengths: the same as packed attention with one query
+    per sequence (end-aligned causal lets it see every cached key), which the
+    varlen oracle computes by a separate path; empty caches give O = 0 and
+    LSE = -inf."""
+    rng = np.random.default_rng(91)
+    B, H, Lcap, d = 4, 3, 40, 8
+    lens = [40, 1, 0, 17]
+    q, k, v = _rand(rng, B, H, 1, d), _rand(rng, B, H, Lcap, d), _rand(rng, B, H, Lcap, d)
+    O, L = oracle.decode_attention_ragged(q, k, v, lens, 0.4)
+    qp = q[:, :, 0].copy()                                          # [B, H, d] = packed [total_q, H, d]
+    kp = np.concatenate([k[b, :, :n].transpose(1, 0, 2) for b, n in enumerate(lens)])
+    vp = np.concatenate([v[b, :, :n].transpose(1, 0, 2) for b, n in enumerate(lens)])
+    Ov, Lv = oracle.attention_varlen(qp, kp, vp, np.arange(B + 1), np.concatenate([[0], np.cumsum(lens)]),
+                                     0.4, causal=True)
+    np.testing.assert_allclose(O[:, :, 0], Ov, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(L[:, :, 0], Lv.T, rtol=0, atol=1e-13)
+    assert np.all(O[2] == 0) and np.all(np.isneginf(L[2]))
+    # full-length caches are plain decode
+    Of, Lf = oracle.decode_attention_ragged(q, k, v, [Lcap] * B, 0.4)
+    Od, Ld = oracle.decode_attention(q, k, v, 0.4)
+    np.testing.assert_array_equal(Of, Od)
+    np.testing.assert_array_equal(Lf, Ld)
