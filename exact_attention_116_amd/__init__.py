@@ -16,7 +16,8 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = ra
 FA_BF16, FA_FP32, FA_FP8_E4M3 = range(3)
 
 EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_decode_splitkv", "fa_decode_workspace_bytes",
-           "fa_decode_splitkv_ex", "fa_decode_splitkv_gqa", "fa_fwd_varlen", "fa_fp8_quantize",
+           "fa_decode_splitkv_ex", "fa_decode_splitkv_gqa", "fa_decode_splitkv_varlen",
+           "fa_fwd_varlen", "fa_fp8_quantize",
            "fa_bwd_workspace_bytes", "fa_bwd",
            "fa_status_string", "fa_last_error")
 
@@ -62,6 +63,8 @@ def load(path: str | None = None):
     lib.fa_decode_splitkv_ex.restype = I
     lib.fa_decode_splitkv_gqa.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, P, Z, P]
     lib.fa_decode_splitkv_gqa.restype = I
+    lib.fa_decode_splitkv_varlen.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, P, Z, P]
+    lib.fa_decode_splitkv_varlen.restype = I
     lib.fa_fwd_varlen.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
     lib.fa_fwd_varlen.restype = I
     lib.fa_fp8_quantize.argtypes = [P, P, P, P, I, I, I, I, P]
@@ -175,3 +178,13 @@ def fa_fp8_quantize(x, signs, codes, scales, B, H, N, d, stream=None):
     """bf16 [B,H,N,d] -> E4M3FN codes + fp32 [B,H,ceil(N/64)] scales; signs [d] rotates."""
     _check(load().fa_fp8_quantize(_ptr(x), _ptr(signs), _ptr(codes), _ptr(scales), B, H, N, d,
                                   _stream(stream)), "fa_fp8_quantize")
+
+
+def fa_decode_splitkv_varlen(q, kcache, vcache, o, lse, seqlens_k, B, Hq, Hkv, Lkv, d, num_splits,
+                             scale, workspace=None, workspace_bytes=0, stream=None):
+    """Grouped decode over padded caches [B,Hkv,Lkv,d] with int32 seqlens_k [B] (device)."""
+    _check(load().fa_decode_splitkv_varlen(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(o),
+                                           _ptr(lse), _ptr(seqlens_k), B, Hq, Hkv, Lkv, d,
+                                           num_splits, float(scale), _ptr(workspace),
+                                           int(workspace_bytes), _stream(stream)),
+           "fa_decode_splitkv_varlen")

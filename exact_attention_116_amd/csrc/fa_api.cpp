@@ -116,15 +116,18 @@ fa_status check_decode(const void* q, const void* kc, const void* vc, const void
 }
 
 // Hkv = 0: plain multi-head decode (one K/V head per query head);
-// Hkv > 0: grouped heads, query head h reads K/V head h / (H / Hkv).
+// Hkv > 0: grouped heads, query head h reads K/V head h / (H / Hkv), and an
+// optional length per sequence (seqlens, device, or null).
 fa_status run_decode(const void* q, const void* kc, const void* vc, void* o, float* lse, int B,
-                     int H, int Hkv, int Lkv, int d, int S, float scale, void* ws, void* stream) {
+                     int H, int Hkv, int Lkv, int d, int S, float scale, void* ws, void* stream,
+                     const int* seqlens = nullptr) {
   fa::DecodeArgs a{};
   a.q = q; a.k = kc; a.v = vc; a.o = o; a.lse = lse;
   a.part_o = static_cast<float*>(ws);
   a.part_lse = static_cast<float*>(ws) + (size_t)B * H * S * d;
   a.B = B; a.H = H; a.Lkv = Lkv; a.d = d; a.num_splits = S;
   a.Hkv = Hkv > 0 ? Hkv : H;
+  a.seqlens_k = seqlens;
   a.scale_log2 = (float)((double)scale * kLog2e);
   a.stream = stream;
   hipError_t e = Hkv > 0 ? fa::launch_decode_gqa(a) : fa::launch_decode(a);
@@ -170,6 +173,33 @@ fa_status owned_workspace(size_t need, void** out) {
   }
   *out = g_ws.ptr[dev];
   return FA_OK;
+}
+
+// The grouped-head decode behind fa_decode_splitkv_gqa and
+// fa_decode_splitkv_varlen (seqlens may be null).
+fa_status decode_grouped(const void* q, const void* kcache, const void* vcache, void* o,
+                         float* lse, const int* seqlens, int B, int Hq, int Hkv, int Lkv, int d,
+                         int num_splits, float scale, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (Hkv < 1 || Hq < 1 || Hq % Hkv != 0)
+    return fail(FA_ERR_INVALID_ARG, "Hkv must be >= 1 and divide Hq");
+  fa_status st = check_decode(q, kcache, vcache, o, B, Hq, Lkv, d, num_splits, scale);
+  if (st != FA_OK) return st;
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  const size_t need = decode_ws_bytes(B, Hq, d, num_splits);
+  void* ws = workspace;
+  if (!workspace) {
+    if (workspace_bytes != 0) return fail(FA_ERR_WORKSPACE, "workspace is NULL but workspace_bytes is not 0");
+    st = owned_workspace(need, &ws);
+    if (st != FA_OK) return st;
+  } else {
+    if (!aligned16(workspace)) return fail(FA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(FA_ERR_WORKSPACE, "workspace smaller than fa_decode_workspace_bytes()");
+  }
+  return run_decode(q, kcache, vcache, o, lse, B, Hq, Hkv, Lkv, d, num_splits, scale, ws, stream,
+                    seqlens);
 }
 
 }  // namespace
@@ -224,25 +254,21 @@ fa_status fa_decode_splitkv(const void* q, const void* kcache, const void* vcach
 fa_status fa_decode_splitkv_gqa(const void* q, const void* kcache, const void* vcache, void* o,
                                 float* lse, int B, int Hq, int Hkv, int Lkv, int d, int num_splits,
                                 float scale, void* workspace, size_t workspace_bytes, void* stream) {
-  if (Hkv < 1 || Hq < 1 || Hq % Hkv != 0)
-    return fail(FA_ERR_INVALID_ARG, "Hkv must be >= 1 and divide Hq");
-  fa_status st = check_decode(q, kcache, vcache, o, B, Hq, Lkv, d, num_splits, scale);
-  if (st != FA_OK) return st;
-  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u))
-    return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-  const size_t need = decode_ws_bytes(B, Hq, d, num_splits);
-  void* ws = workspace;
-  if (!workspace) {
-    if (workspace_bytes != 0) return fail(FA_ERR_WORKSPACE, "workspace is NULL but workspace_bytes is not 0");
-    st = owned_workspace(need, &ws);
-    if (st != FA_OK) return st;
-  } else {
-    if (!aligned16(workspace)) return fail(FA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-    if (workspace_bytes < need)
-      return fail(FA_ERR_WORKSPACE, "workspace smaller than fa_decode_workspace_bytes()");
-  }
-  return run_decode(q, kcache, vcache, o, lse, B, Hq, Hkv, Lkv, d, num_splits, scale, ws, stream);
+  return decode_grouped(q, kcache, vcache, o, lse, nullptr, B, Hq, Hkv, Lkv, d, num_splits, scale,
+                        workspace, workspace_bytes, stream);
 }
+
+fa_status fa_decode_splitkv_varlen(const void* q, const void* kcache, const void* vcache, void* o,
+                                   float* lse, const int* seqlens_k, int B, int Hq, int Hkv,
+                                   int Lkv, int d, int num_splits, float scale, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (!seqlens_k || (reinterpret_cast<uintptr_t>(seqlens_k) & 3u))
+    return fail(FA_ERR_INVALID_ARG, "seqlens_k must be non-NULL and 4-byte aligned");
+  return decode_grouped(q, kcache, vcache, o, lse, seqlens_k, B, Hq, Hkv, Lkv, d, num_splits,
+                        scale, workspace, workspace_bytes, stream);
+}
+
+
 
 fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                         const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H,

@@ -9,7 +9,9 @@
 // acceleration V6" page: keys and values keep one shared head, queries keep
 // all of theirs).  One workgroup takes one (batch, K/V head, split) and up to
 // 16 (groups of at most 16) or 32 (larger groups) of the query heads that
-// share it, so every cached byte it streams serves all of them.
+// share it, so every cached byte it streams serves all of them.  With a
+// length per sequence, sequence b uses the first seqlens[b] keys of its
+// padded cache, split into num_splits ranges of its own.
 //
 // gfx950 mapping: the G queries of a group make both products small dense
 // contractions, so they run on v_mfma_f32_16x16x32_bf16 with the query heads
@@ -35,8 +37,9 @@ template <int D, int NW, int U, int QB>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 void fa_decode_gqa_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
                                 const bf16* __restrict__ vc, float* __restrict__ part_o,
-                                float* __restrict__ part_lse, int Hq, int Hkv, int G, int QC,
-                                int Lkv, int S, int chunk, float c) {
+                                float* __restrict__ part_lse, const int* __restrict__ seqlens,
+                                int Hq, int Hkv, int G, int QC, int Lkv, int S, int chunk,
+                                float c) {
   static_assert(D == 64 || D == 128, "head dimension 64 or 128");
   constexpr int KT = D / 32;    // k-steps of the score product
   constexpr int NB = D / 16;    // 16-feature blocks of the output; also features per lane of a V row
@@ -57,9 +60,16 @@ void fa_decode_gqa_split_kernel(const bf16* __restrict__ q, const bf16* __restri
   const int h0 = hk * G + qc * NH;
   const int gc = (G - qc * NH) < NH ? (G - qc * NH) : NH;  // query heads of this workgroup
 
+  // keys of this sequence: all Lkv, or its own length within the padded
+  // cache, cut into S splits of ceil(length / S)
+  int Lb = Lkv;
+  if (seqlens) {
+    Lb = min(max(seqlens[b], 0), Lkv);
+    chunk = (Lb + S - 1) / S;
+  }
   const long long lo_ll = (long long)s * chunk;
-  const int lo = (int)(lo_ll < Lkv ? lo_ll : Lkv);
-  const int hi = (int)((long long)lo + chunk < Lkv ? (long long)lo + chunk : Lkv);
+  const int lo = (int)(lo_ll < Lb ? lo_ll : Lb);
+  const int hi = (int)((long long)lo + chunk < Lb ? (long long)lo + chunk : Lb);
   const int nkeys = hi - lo;
 
   // Q^T as the B operand of the score product: column n of block qq is query
@@ -234,8 +244,8 @@ static hipError_t launch_gqa_cfg(const DecodeArgs& a) {
   const long long grid = (long long)a.B * a.Hkv * QC * a.num_splits;
   hipLaunchKernelGGL((fa_decode_gqa_split_kernel<D, NW, U, QB>), dim3((unsigned)grid), dim3(NW * 64),
                      0, (hipStream_t)a.stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
-                     a.part_o, a.part_lse, a.H, a.Hkv, G, QC, a.Lkv, a.num_splits, chunk,
-                     a.scale_log2);
+                     a.part_o, a.part_lse, a.seqlens_k, a.H, a.Hkv, G, QC, a.Lkv, a.num_splits,
+                     chunk, a.scale_log2);
   return hipGetLastError();
 }
 

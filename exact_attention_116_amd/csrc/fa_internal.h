@@ -42,6 +42,7 @@ struct DecodeArgs {
   float* part_lse;    // [B*H, S]    fp32
   int B, H, Lkv, d, num_splits;
   int Hkv;            // key/value heads (H for plain multi-head decode)
+  const int* seqlens_k;  // [B] keys per sequence in the padded cache, or null (all Lkv)
   float scale_log2;
   void* stream;
 };

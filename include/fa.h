@@ -173,6 +173,23 @@ fa_status fa_decode_splitkv_gqa(const void* q, const void* kcache, const void* v
                                 size_t workspace_bytes, void* stream);
 
 /*
+ * fa_decode_splitkv_varlen -- fa_decode_splitkv_gqa over a padded cache with
+ * a length per sequence (a serving batch whose sequences have different
+ * numbers of cached tokens): sequence b attends over the first
+ * Lb = seqlens_k[b] keys of its cache (clamped to [0, Lkv]).  Its keys are
+ * cut into num_splits ranges of c_b = ceil(Lb / num_splits): split s covers
+ * [s*c_b, min((s+1)*c_b, Lb)).  A sequence with Lb = 0 gets O = 0 and
+ * LSE = -inf.
+ *
+ * seqlens_k : int32 DEVICE array [B]; kcache, vcache : bf16 [B, Hkv, Lkv, d]
+ * (Lkv the capacity).  Everything else as fa_decode_splitkv_gqa.
+ */
+fa_status fa_decode_splitkv_varlen(const void* q, const void* kcache, const void* vcache, void* o,
+                                   float* lse, const int* seqlens_k, int B, int Hq, int Hkv,
+                                   int Lkv, int d, int num_splits, float scale, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
  * fa_fwd_varlen -- the bf16 forward pass over a batch of packed sequences of
  * unequal lengths (the power-of-two length rule of the Flash Attention
  * note, "使用注意事项", does not apply: any lengths work).  Sequence b has

@@ -188,6 +188,24 @@ def test_fp8_quantize_rejects(lib, kw, status):
     assert st == status
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(seq=None), fa.FA_ERR_INVALID_ARG),
+    (dict(seq=A + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(Hkv=3), fa.FA_ERR_INVALID_ARG),
+    (dict(S=17), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(ws=A, ws_bytes=64), fa.FA_ERR_WORKSPACE),
+])
+def test_decode_varlen_rejects(lib, kw, status):
+    a = dict(q=A, kc=A, vc=A, o=A, lse=None, seq=A, B=2, Hq=8, Hkv=2, Lkv=16, d=128, S=4,
+             scale=0.1, ws=None, ws_bytes=0)
+    a.update(kw)
+    st = lib.fa_decode_splitkv_varlen(a["q"], a["kc"], a["vc"], a["o"], a["lse"], a["seq"], a["B"],
+                                      a["Hq"], a["Hkv"], a["Lkv"], a["d"], a["S"], a["scale"],
+                                      a["ws"], a["ws_bytes"], None)
+    assert st == status
+
+
 def test_binding_raises_with_status():
     with pytest.raises(fa.FaError) as e:
         fa.fa_fwd(A, A, A, A, None, 1, 1, 16, 128, 0.1, False)

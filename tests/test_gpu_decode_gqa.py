@@ -143,3 +143,77 @@ def test_gqa_deterministic_and_in_bounds(gpu_lib):
     assert torch.equal(outs[0][1], outs[1][1])
     for buf, n in ((obuf, nel), (lbuf, B * Hq), (wbuf, need // 4)):
         assert torch.all(buf[:Gd] == 7.0) and torch.all(buf[Gd + n:] == 7.0)
+
+
+# ---------------------------------------------------------------------------
+# a length per sequence in a padded cache
+# ---------------------------------------------------------------------------
+
+def run_varlen(fa, q, k, v, lens, B, Hq, Hkv, Lkv, d, S, scale):
+    o = torch.empty((B, Hq, 1, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    nbytes = fa.fa_decode_workspace_bytes(B, Hq, d, S)
+    ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    fa.fa_decode_splitkv_varlen(q, k, v, o, lse, sl, B, Hq, Hkv, Lkv, d, S, scale, ws, nbytes)
+    torch.cuda.synchronize()
+    po = ws[:B * Hq * S * d].view(B, Hq, S, d)
+    pl = ws[B * Hq * S * d:B * Hq * S * (d + 1)].view(B, Hq, S)
+    return o, lse, po, pl
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2), (40, 2)])
+@pytest.mark.parametrize("S", [1, 7, 64])
+def test_varlen_decode_small(gpu_lib, S, Hq, Hkv, d):
+    fa = gpu_lib
+    Lkv = 3000
+    lens = [3000, 1, 0, 5, 2999, 64, 1000, 63]
+    B = len(lens)
+    wid = 6800 + S + Hq + Hkv + d
+    say(f"varlen decode lens={lens} Hq={Hq} Hkv={Hkv} d={d} splits={S} seed-id={wid}")
+    qb, kb, vb = gen(wid, B, Hq, Hkv, Lkv, d)
+    # padding past each sequence's length holds garbage the kernel must not read
+    for b, n in enumerate(lens):
+        kb[b, :, n:] = 0x7F80   # +inf in bf16
+        vb[b, :, n:] = 0x7FC0   # NaN
+    scale = d ** -0.5
+    o, lse, po, pl = run_varlen(fa, *map(bf16_to_dev, (qb, kb, vb)), lens, B, Hq, Hkv, Lkv, d, S,
+                                scale)
+    q, k, v = map(oracle.decode_bf16, (qb, kb, vb))
+    O, L = oracle.decode_attention_ragged(q, k, v, lens, scale)
+    og, lg = dev_to_f64(o)[:, :, 0], dev_to_f64(lse)
+    empty = np.array([n == 0 for n in lens])
+    assert np.all(og[empty] == 0) and np.all(np.isneginf(lg[empty]))
+    check_bf16_gates(og[~empty], O[~empty, :, 0], lg[~empty], L[~empty, :, 0], "merged",
+                     beyond_floor=True)
+    pog, plg = dev_to_f64(po), dev_to_f64(pl)
+    kv_of = np.arange(Hq) // (Hq // Hkv)
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert np.all(np.isneginf(plg[b])) and np.all(pog[b] == 0)
+            continue
+        Os, Ls = oracle.split_partials(q[b], k[b, kv_of, :n], v[b, kv_of, :n], scale, S)
+        e = np.isneginf(Ls[:, :, 0])
+        assert np.array_equal(np.isneginf(plg[b]), e)
+        assert np.abs(pog[b] - Os[:, :, 0]).max() <= 1e-2
+
+
+def test_varlen_decode_serving_batch(gpu_lib):
+    """A serving-style batch over a 64 Ki-token padded cache: B=8, Hq=64,
+    Hkv=8, d=128, 64 splits, sequence lengths from 1 to 65536; sampled heads
+    against the oracle."""
+    fa = gpu_lib
+    lens = [65536, 1000, 30000, 7, 65535, 4096, 300, 50000]
+    B, Hq, Hkv, Lkv, d, S = 8, 64, 8, 65536, 128, 64
+    say("varlen decode serving batch: generating")
+    qb, kb, vb = gen(6900, B, Hq, Hkv, Lkv, d)
+    o, lse, _, _ = run_varlen(fa, *map(bf16_to_dev, (qb, kb, vb)), lens, B, Hq, Hkv, Lkv, d, S,
+                              d ** -0.5)
+    og, lg = dev_to_f64(o), dev_to_f64(lse)
+    for b, h in [(0, 0), (1, 9), (3, 63), (4, 17), (6, 40), (7, 8)]:
+        n = lens[b]
+        Q = oracle.decode_bf16(qb[b, h])
+        K, V = (oracle.decode_bf16(x[b, h // 8, :n]) for x in (kb, vb))
+        O, L = oracle.decode_attention(Q, K, V, d ** -0.5)
+        check_bf16_gates(og[b, h], O, lg[b, h:h + 1], L, f"(b={b},h={h},len={n})")
