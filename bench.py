@@ -58,13 +58,13 @@ TRAFFIC_KIB = {
            "write_kib": (8706.0 + 8707.0 + 8705.0) / 3 + 72.0,
            "sha256": "981ba075afae4656b287e80ae205d6e3aee2a77c8eb71461d5f88c70436e85ce"},
     "c6": {"src": ["fa_decode_gqa.hip", "fa_decode.hip"],
-           "fetch_kib": (1086608.0 + 1087127.0 + 1087528.0) / 3 + (8342.0 + 8340.0 + 8340.0) / 3,
-           "write_kib": (17410.0 + 17409.0 + 17410.0) / 3 + 144.0,
-           "sha256": "b13a0363f2e352b24df6af9f7e4f1c62d153cac0dfccbd62f457a23bc8ba756b"},
+           "fetch_kib": (1085756.0 + 1086890.0 + 1087423.0) / 3 + (8342.0 + 8340.0 + 8340.0) / 3,
+           "write_kib": (17408.0 + 17411.0 + 17411.0) / 3 + 144.0,
+           "sha256": "25954e349dc11628f133e3705649a35da2f735b0ceb1901d0f6bfd698adea4f5"},
     "c7": {"src": ["fa_decode_gqa.hip", "fa_decode.hip"],
-           "fetch_kib": (132968.0 + 133160.0 + 132813.0) / 3 + (4182.0 + 4180.0 + 4180.0) / 3,
-           "write_kib": (8704.0 + 8705.0 + 8704.0) / 3 + 72.0,
-           "sha256": "b13a0363f2e352b24df6af9f7e4f1c62d153cac0dfccbd62f457a23bc8ba756b"},
+           "fetch_kib": (132958.0 + 132912.0 + 133009.0) / 3 + (4182.0 + 4180.0 + 4180.0) / 3,
+           "write_kib": 8704.0 + 72.0,
+           "sha256": "25954e349dc11628f133e3705649a35da2f735b0ceb1901d0f6bfd698adea4f5"},
 }
 
 
