@@ -4,7 +4,10 @@
 One step = one pass of the whole hot path over resident synthetic inputs:
   * bf16 forward, B=2 H=32 N=2048 d=128, causal and non-causal
   * bf16 forward, B=1 H=16 N=16384 d=128, causal
-  * split-KV decode, B=8 H=32 Lkv=65536 d=128, 64 splits (split + merge kernels)
+  * split-KV decode, B=8 H=32 Lkv=65536 d=128, 64 splits (split + merge kernels),
+    and for context the same with one split, and one sequence of it (B=1)
+    with 64 splits and with one: what splitting the KV length buys on this
+    GPU (with 256 (b,h) pairs every CU already has work; with 32 it does not)
   * split-KV decode with grouped K/V heads, B=8 Lkv=65536 d=128, 64 splits:
     Hq=64 over Hkv=8 (GQA), and Hq=32 over one K/V head (MQA)
   * bf16 -> block-scaled fp8 quantisation of the fp8 workload's Q and K
@@ -114,7 +117,7 @@ def cpu_info():
             if line.startswith("model name"):
                 model = line.split(":", 1)[1].strip()
                 break
-    except OSError:
+    except (OSError, AttributeError):
         pass
     return model
 
@@ -155,6 +158,7 @@ def cpu_baseline(seconds):
         pairs += 1
     return {
         "value": flops / t_fwd / 1e12,
+        "value_full_s": 2 * flops / t_fwd / 1e12,   # the oracle materialises all of S, masked or not
         "unit": "TFLOPS",
         "cores": threads,
         "kind": "oracle",
@@ -177,7 +181,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", default="all",
-                    help="all | c2c | c2n | c3 | c4 | c5 | q5 | c6 | c7 | c8 | b2c | b3 (profiling)")
+                    help="all | c2c | c2n | c3 | c4 | c4s1 | c5 | q5 | c6 | c7 | c8 | b2c | b3 "
+                         "(profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy per step (for HBM counter scaling)")
     args = ap.parse_args()
@@ -222,7 +227,7 @@ def main():
         jobs.append(("c3", lambda: fa.fa_fwd_ex(q3, k3, v3, o3, l3, w3.B, w3.H, w3.N, w3.d,
                                                 w3.scale, True, stream=stream),
                      fwd_flops(w3, True), fwd_bytes(w3), "fwd_bf16"))
-    if want("c4"):
+    if want("c4") or want("c4s1"):
         log("generating decode B=8 H=32 Lkv=65536 d=128 inputs (8 GiB)")
         q4 = up_bf16(fi.bf16_tensor(w4.wid, 0, w4.B, w4.H, 1, w4.d))
         k4 = up_bf16(fi.bf16_tensor(w4.wid, 1, w4.B, w4.H, w4.Lkv, w4.d))
@@ -231,9 +236,22 @@ def main():
         l4 = torch.empty((w4.B, w4.H), dtype=torch.float32, device=dev)
         wsb = fa.fa_decode_workspace_bytes(w4.B, w4.H, w4.d, w4.num_splits)
         ws4 = torch.empty(wsb // 4, dtype=torch.float32, device=dev)
-        jobs.append(("c4", lambda: fa.fa_decode_splitkv_ex(
-            q4, k4, v4, o4, l4, w4.B, w4.H, w4.Lkv, w4.d, w4.num_splits, w4.scale, ws4, wsb,
-            stream=stream), 4.0 * w4.B * w4.H * w4.Lkv * w4.d, decode_bytes(w4), "decode"))
+        if want("c4"):
+            jobs.append(("c4", lambda: fa.fa_decode_splitkv_ex(
+                q4, k4, v4, o4, l4, w4.B, w4.H, w4.Lkv, w4.d, w4.num_splits, w4.scale, ws4, wsb,
+                stream=stream), 4.0 * w4.B * w4.H * w4.Lkv * w4.d, decode_bytes(w4), "decode"))
+        if args.only == "all":
+            # one sequence (the first batch row, a contiguous view) with 64 splits and with 1
+            q1, k1, v1, o1, l1 = q4[:1], k4[:1], v4[:1], o4[:1], l4[:1]
+            for tag, S1 in (("c4b1", w4.num_splits), ("c4b1s1", 1)):
+                jobs.append((tag, (lambda S1=S1: fa.fa_decode_splitkv_ex(
+                    q1, k1, v1, o1, l1, 1, w4.H, w4.Lkv, w4.d, S1, w4.scale, ws4, wsb,
+                    stream=stream)), 4.0 * w4.H * w4.Lkv * w4.d, decode_bytes(w4) // w4.B,
+                    "decode"))
+        if want("c4s1"):
+            jobs.append(("c4s1", lambda: fa.fa_decode_splitkv_ex(
+                q4, k4, v4, o4, l4, w4.B, w4.H, w4.Lkv, w4.d, 1, w4.scale, ws4, wsb,
+                stream=stream), 4.0 * w4.B * w4.H * w4.Lkv * w4.d, decode_bytes(w4), "decode"))
     for tag, wid in (("c6", 6), ("c7", 7)):
         if not want(tag):
             continue
@@ -406,6 +424,14 @@ def main():
     if "c4" in res:
         g = res["c4"]["gbs"]
         decode = {"value": g, "unit": "GB/s", "ms": res["c4"]["ms_mean"],
+                  "one_split": ({"value": res["c4s1"]["gbs"], "ms": res["c4s1"]["ms_mean"],
+                                 "speedup_of_64_splits": res["c4s1"]["ms_mean"] / res["c4"]["ms_mean"]}
+                                if "c4s1" in res else None),
+                  "one_sequence": ({"workload": "B=1 H=32 Lkv=65536 d=128",
+                                    "value_64_splits": res["c4b1"]["gbs"],
+                                    "value_1_split": res["c4b1s1"]["gbs"],
+                                    "speedup_of_64_splits": res["c4b1s1"]["ms_mean"] / res["c4b1"]["ms_mean"]}
+                                   if "c4b1" in res else None),
                   "roofline": {"kernel": "fa_decode_split_kernel + fa_decode_combine_kernel",
                                "bound": "hbm", "achieved": g, "peak": PEAK_HBM_GBS,
                                "unit": "GB/s", "frac": g / PEAK_HBM_GBS,
@@ -456,6 +482,16 @@ def main():
                                           "frac": a / PEAK_BF16_TFLOPS, "traffic": None,
                                           "algorithmic_bytes": res[tag]["bytes"]}}
     prop = torch.cuda.get_device_properties(0)
+    clock_khz = None
+    try:   # hipDeviceAttributeClockRate (kHz), from the HIP runtime torch already loaded
+        import ctypes
+        hip = ctypes.CDLL("libamdhip64.so")
+        val = ctypes.c_int(0)
+        attr_clock_rate = 5   # hipDeviceAttributeClockRate
+        if hip.hipDeviceGetAttribute(ctypes.byref(val), attr_clock_rate, 0) == 0:
+            clock_khz = val.value
+    except (OSError, AttributeError):
+        pass
     out = {
         "metric": METRIC,
         "value": value,
@@ -484,7 +520,7 @@ def main():
         "backward": backward or None,
         "workloads": res,
         "device": {"name": prop.name, "cus": prop.multi_processor_count,
-                   "gcn_arch": getattr(prop, "gcnArchName", "")},
+                   "gcn_arch": getattr(prop, "gcnArchName", ""), "clock_khz": clock_khz},
         "wall_s_timed": wall,
     }
     log(f"timed {args.steps} steps in {wall:.2f} s")
