@@ -38,7 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "fwd TFLOPS (bf16 causal, N=2K-16K) + split-KV decode HBM GB/s, 1 GPU"
-PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk)
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 (and fp16) MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk)
 PEAK_FP8_TFLOPS = 5033.2      # dense fp8
 PEAK_HBM_GBS = 8000.0
 
@@ -49,25 +49,26 @@ PEAK_HBM_GBS = 8000.0
 # written, so fetches are scaled by 1048576/524300 and writes by 1.  Each
 # entry is tied to the SHA-256 of its kernel source plus the shared device
 # header: once either changes, the figure no longer describes the kernel and
-# the bench reports traffic as null.  Split-KV decode entries add the
+# the bench reports traffic as null.  (A digest is moved to a new source only
+# when the measured kernels' instructions were compared and found identical.)  Split-KV decode entries add the
 # split-merge kernel's counters to the split kernel's.
 COUNTER_SCALE = {"fetch": 1048576.0 / 524300.0, "write": 1.0}
 TRAFFIC_KIB = {
     "c3": {"src": ["fa_fwd_bf16.hip"], "fetch_kib": (257391.0 + 247438.0 + 264977.0) / 3,
            "write_kib": 66560.0,
-           "sha256": "fbd8adce8d194650079a59af12a8c67212e0222eefade8fc9ab65323d8d2266d"},
+           "sha256": "e763869c6944be397367e44a7ad0863455ce8d2d3ebed206139fc62bb6a99d6b"},
     "c4": {"src": ["fa_decode.hip"],
            "fetch_kib": (4194784.0 + 4194625.0 + 4194618.0) / 3 + 4180.0,
            "write_kib": (8706.0 + 8707.0 + 8705.0) / 3 + 72.0,
-           "sha256": "981ba075afae4656b287e80ae205d6e3aee2a77c8eb71461d5f88c70436e85ce"},
+           "sha256": "68354608e0cfa829b4d3586aec42625d81df5ad26ffc40923d1d4ff0a0423f73"},
     "c6": {"src": ["fa_decode_gqa.hip", "fa_decode.hip"],
            "fetch_kib": (1085756.0 + 1086890.0 + 1087423.0) / 3 + (8342.0 + 8340.0 + 8340.0) / 3,
            "write_kib": (17408.0 + 17411.0 + 17411.0) / 3 + 144.0,
-           "sha256": "25954e349dc11628f133e3705649a35da2f735b0ceb1901d0f6bfd698adea4f5"},
+           "sha256": "5db09feb3690d30c67d7521a98a025ef0093a915e2042f2be6961e33cf87e22e"},
     "c7": {"src": ["fa_decode_gqa.hip", "fa_decode.hip"],
            "fetch_kib": (132958.0 + 132912.0 + 133009.0) / 3 + (4182.0 + 4180.0 + 4180.0) / 3,
            "write_kib": 8704.0 + 72.0,
-           "sha256": "25954e349dc11628f133e3705649a35da2f735b0ceb1901d0f6bfd698adea4f5"},
+           "sha256": "5db09feb3690d30c67d7521a98a025ef0093a915e2042f2be6961e33cf87e22e"},
 }
 
 
@@ -181,7 +182,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", default="all",
-                    help="all | c2c | c2n | c3 | c4 | c4s1 | c5 | q5 | c6 | c7 | c8 | b2c | b3 "
+                    help="all | c2c | c2n | c3 | c3h | c4 | c4s1 | c5 | q5 | c6 | c7 | c8 | b2c | b3 "
                          "(profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy per step (for HBM counter scaling)")
@@ -227,6 +228,16 @@ def main():
         jobs.append(("c3", lambda: fa.fa_fwd_ex(q3, k3, v3, o3, l3, w3.B, w3.H, w3.N, w3.d,
                                                 w3.scale, True, stream=stream),
                      fwd_flops(w3, True), fwd_bytes(w3), "fwd_bf16"))
+    if want("c3h"):
+        log("generating B=1 H=16 N=16384 d=128 fp16 inputs")
+        q3h, k3h, v3h = (torch.from_numpy(fi.f16_tensor(w3.wid, t, w3.B, w3.H, w3.N, w3.d).view(np.int16))
+                         .view(torch.float16).to(dev) for t in range(3))
+        o3h = torch.empty_like(q3h)
+        l3h = torch.empty((w3.B, w3.H, w3.N), dtype=torch.float32, device=dev)
+        jobs.append(("c3h", lambda: fa.fa_fwd_ex(q3h, k3h, v3h, o3h, l3h, w3.B, w3.H, w3.N, w3.d,
+                                                 w3.scale, True, in_dtype=fa.FA_FP16,
+                                                 out_dtype=fa.FA_FP16, stream=stream),
+                     fwd_flops(w3, True), fwd_bytes(w3), "fwd_fp16"))
     if want("c4") or want("c4s1"):
         log("generating decode B=8 H=32 Lkv=65536 d=128 inputs (8 GiB)")
         q4 = up_bf16(fi.bf16_tensor(w4.wid, 0, w4.B, w4.H, 1, w4.d))
@@ -460,6 +471,15 @@ def main():
                                "achieved": a, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                "frac": a / PEAK_BF16_TFLOPS, "traffic": None,
                                "algorithmic_bytes": res["c8"]["bytes"]}}
+    fp16 = None
+    if "c3h" in res:
+        a = res["c3h"]["tflops"]
+        fp16 = {"workload": w3.name + " causal, fp16 inputs and output", "value": a, "unit": "TFLOPS",
+                "ms": res["c3h"]["ms_mean"],
+                "roofline": {"kernel": "fa_fwd_bf16_kernel (fp16 instance)", "bound": "mfma",
+                             "achieved": a, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                             "frac": a / PEAK_BF16_TFLOPS, "traffic": None,
+                             "algorithmic_bytes": res["c3h"]["bytes"]}}
     quant = None
     if "q5" in res:
         g = res["q5"]["gbs"]
@@ -510,13 +530,15 @@ def main():
                                "grouped decode B8 Hq64/Hkv8 and Hq32/Hkv1 Lkv65536 (decode_gqa); "
                                "causal backward of B2H32N2048d128 and B1H16N16384d128 (backward); "
                                "ragged chunked prefill of 8 packed sequences H32d128 (varlen_prefill); "
-                               "bf16->fp8 quantisation of the fp8 workload (fp8_quantize)",
+                               "bf16->fp8 quantisation of the fp8 workload (fp8_quantize); "
+                               "fp16 causal fwd B1H16N16384d128 (fp16_prefill)",
                    "only": args.only},
         "roofline": roof,
         "decode": decode,
         "decode_gqa": decode_gqa or None,
         "varlen_prefill": varlen,
         "fp8_quantize": quant,
+        "fp16_prefill": fp16,
         "backward": backward or None,
         "workloads": res,
         "device": {"name": prop.name, "cus": prop.multi_processor_count,

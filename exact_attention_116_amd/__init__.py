@@ -13,7 +13,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
-FA_BF16, FA_FP32, FA_FP8_E4M3 = range(3)
+FA_BF16, FA_FP32, FA_FP8_E4M3, FA_FP16 = range(4)
 
 EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_decode_splitkv", "fa_decode_workspace_bytes",
            "fa_decode_splitkv_ex", "fa_decode_splitkv_gqa", "fa_decode_splitkv_varlen",

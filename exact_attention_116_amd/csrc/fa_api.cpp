@@ -43,8 +43,8 @@ fa_status check_fwd(const fa_fwd_params* p) {
     return fail(FA_ERR_INVALID_ARG, "B, H and N must be >= 1");
   if (p->d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1");
   if (!good_scale(p->scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
-  if (p->out_dtype != FA_BF16 && p->out_dtype != FA_FP32)
-    return fail(FA_ERR_INVALID_ARG, "out_dtype must be FA_BF16 or FA_FP32");
+  if (p->out_dtype != FA_BF16 && p->out_dtype != FA_FP32 && p->out_dtype != FA_FP16)
+    return fail(FA_ERR_INVALID_ARG, "out_dtype must be FA_BF16, FA_FP16 or FA_FP32");
   const long long elems = (long long)p->B * p->H * p->N * p->d;
   if ((long long)p->B * p->H * ((p->N + 31) / 32) > 0x7FFFFFFFLL || elems <= 0)
     return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
@@ -52,10 +52,12 @@ fa_status check_fwd(const fa_fwd_params* p) {
   const long long elem_bytes = p->in_dtype == FA_FP8_E4M3 ? 1 : 2;
   if ((long long)p->N * p->d * elem_bytes >= (1LL << 32))
     return fail(FA_ERR_UNSUPPORTED, "one (batch, head) slice must be smaller than 4 GiB");
-  if (p->in_dtype == FA_BF16) {
+  if (p->in_dtype == FA_BF16 || p->in_dtype == FA_FP16) {
     if (p->q_scale || p->k_scale || p->v_scale)
       return fail(FA_ERR_INVALID_ARG, "block scales are only accepted with FA_FP8_E4M3 inputs");
-    if (p->d != 64 && p->d != 128) return fail(FA_ERR_UNSUPPORTED, "bf16 path supports d = 64 or 128");
+    if (p->out_dtype != FA_FP32 && p->out_dtype != p->in_dtype)
+      return fail(FA_ERR_INVALID_ARG, "16-bit inputs write o in their own type or in fp32");
+    if (p->d != 64 && p->d != 128) return fail(FA_ERR_UNSUPPORTED, "16-bit path supports d = 64 or 128");
     return FA_OK;
   }
   if (p->in_dtype == FA_FP8_E4M3) {
@@ -68,7 +70,7 @@ fa_status check_fwd(const fa_fwd_params* p) {
     if (p->out_dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "fp8 path writes bf16 output");
     return FA_OK;
   }
-  return fail(FA_ERR_INVALID_ARG, "in_dtype must be FA_BF16 or FA_FP8_E4M3");
+  return fail(FA_ERR_INVALID_ARG, "in_dtype must be FA_BF16, FA_FP16 or FA_FP8_E4M3");
 }
 
 fa_status run_fwd(const fa_fwd_params* p) {
@@ -82,6 +84,7 @@ fa_status run_fwd(const fa_fwd_params* p) {
   a.scale_log2 = (float)((double)p->scale * kLog2e);
   a.causal = p->causal != 0;
   a.out_f32 = p->out_dtype == FA_FP32;
+  a.in_f16 = p->in_dtype == FA_FP16;
   a.stream = p->stream;
   a.cu_q = nullptr;
   a.cu_k = nullptr;

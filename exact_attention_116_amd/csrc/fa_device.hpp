@@ -16,6 +16,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegInf = -__builtin_inff();
@@ -29,6 +31,13 @@ __device__ __forceinline__ uint32_t as_u32(float x) { return __builtin_bit_cast(
 // holds column l%32, rows 8*(i/4) + 4*(l/32) + i%4 for i = 0..15.
 __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// The same product on IEEE fp16 operands: the eight halves of a lane travel
+// in the same 16 bytes (bf16x8 is used as the carrier of 16-bit bits).
+__device__ __forceinline__ f32x16 mfma32x32x16_f16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                c, 0, 0, 0);
 }
 
 // D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16).  Lane l supplies row
@@ -120,6 +129,24 @@ __device__ __forceinline__ u32x2 buf_load8_nt(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   bf16x2 p = {(bf16)a, (bf16)b};
   return __builtin_bit_cast(uint32_t, p);
+}
+
+// Round two floats to fp16 (nearest even) and pack them (a in the low half).
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  f16x2 p = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+// The 16-bit element type of a forward pass: bf16, or fp16 when F16.
+template <bool F16>
+__device__ __forceinline__ f32x16 mma16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  if constexpr (F16) return mfma32x32x16_f16(a, b, c);
+  else return mfma32x32x16(a, b, c);
+}
+template <bool F16>
+__device__ __forceinline__ uint32_t pack16(float a, float b) {
+  if constexpr (F16) return pack_f16(a, b);
+  else return pack_bf16(a, b);
 }
 
 }  // namespace fa

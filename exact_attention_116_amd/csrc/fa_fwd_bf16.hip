@@ -40,6 +40,11 @@
 //  * Causal: key tiles entirely above the diagonal are never loaded; within
 //    a workgroup, a wave whose 32 queries all precede a tile skips its math;
 //    masking is applied only on tiles that straddle the diagonal or N.
+//  * IEEE fp16 inputs (F16) take the same path with the fp16 MFMA: the
+//    layouts, swizzles and transposing reads only see 16-bit elements.  P is
+//    then rounded to fp16 (at most 2^8 under the lazy rescale, so in range;
+//    terms below 2^-24 of the reference are lost from P*V but not from l)
+//    and O is stored as fp16 unless fp32 output is asked for.
 //  * Packed batches of unequal lengths use the same kernel with runtime
 //    strides: each workgroup finds its sequence's query and key rows from
 //    the cumulative lengths, and causal masking is aligned at the sequence
@@ -73,7 +78,7 @@ struct FwdLayout {
   int H, N, Nk, total_q, total_k;   // N, Nk: longest query / key sequence
 };
 
-template <int D, int BC, int NW, bool CAUSAL, bool OUT_F32>
+template <int D, int BC, int NW, bool CAUSAL, bool OUT_F32, bool F16>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
@@ -222,7 +227,7 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           }
           if (i >= PDK) {
             const int x = i - PDK, u = x / NB, b = x % NB;
-            s[b] = mfma32x32x16(kf[x], qb[u], s[b]);
+            s[b] = mma16<F16>(kf[x], qb[u], s[b]);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -270,7 +275,7 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         for (int h = 0; h < 4; ++h) {
           const float p0 = __builtin_amdgcn_exp2f(fmaf(s[t >> 1][8 * (t & 1) + 2 * h], c, -mref));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(s[t >> 1][8 * (t & 1) + 2 * h + 1], c, -mref));
-          w[h] = pack_bf16(p0, p1);
+          w[h] = pack16<F16>(p0, p1);
           l += p0 + p1;
         }
         pb[t] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
@@ -296,7 +301,7 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           }
           if (i >= PDV) {
             const int x = i - PDV, t = x / NC, cb = x % NC;
-            acc[cb] = mfma32x32x16(vf[x], pb[t], acc[cb]);
+            acc[cb] = mma16<F16>(vf[x], pb[t], acc[cb]);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -324,20 +329,20 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           *reinterpret_cast<f32x4*>(static_cast<float*>(o) + orow + d0) = f32x4{o0, o1, o2, o3};
         } else {
           *reinterpret_cast<u32x2*>(static_cast<bf16*>(o) + orow + d0) =
-              u32x2{pack_bf16(o0, o1), pack_bf16(o2, o3)};
+              u32x2{pack16<F16>(o0, o1), pack16<F16>(o2, o3)};
         }
       }
     if (g == 0) lse[lbase + my_q] = l > 0.f ? (m + __builtin_amdgcn_logf(l)) * kLn2 : kNegInf;
   }
 }
 
-template <int D, int BC, int NW, bool CAUSAL, bool OUT_F32>
+template <int D, int BC, int NW, bool CAUSAL, bool OUT_F32, bool F16>
 static hipError_t launch(const FwdArgs& a) {
   using C = FwdCfg<D, BC, NW>;
   const int nqt = (a.N + C::BR - 1) / C::BR;   // of the longest sequence
   const long long blocks = (long long)nqt * a.B * a.H;
   const FwdLayout lay{a.cu_q, a.cu_k, a.H, a.N, a.Nk, a.total_q, a.total_k};
-  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, BC, NW, CAUSAL, OUT_F32>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, BC, NW, CAUSAL, OUT_F32, F16>), dim3((unsigned)blocks),
                      dim3(C::NT), 0, (hipStream_t)a.stream, (const bf16*)a.q, (const bf16*)a.k,
                      (const bf16*)a.v, a.o, a.lse, a.B * a.H, lay, a.scale_log2);
   return hipGetLastError();
@@ -345,7 +350,8 @@ static hipError_t launch(const FwdArgs& a) {
 
 template <int D, bool CAUSAL, bool OUT_F32>
 static hipError_t launch_d(const FwdArgs& a) {
-  return launch<D, 128, 8, CAUSAL, OUT_F32>(a);
+  if (a.in_f16) return launch<D, 128, 8, CAUSAL, OUT_F32, true>(a);
+  return launch<D, 128, 8, CAUSAL, OUT_F32, false>(a);
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {

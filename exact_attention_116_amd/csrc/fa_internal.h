@@ -29,6 +29,7 @@ struct FwdArgs {
   const int* cu_k;
   int Nk, total_q, total_k;
   int out_f32;
+  int in_f16;         // q, k, v (and a 16-bit o) are IEEE fp16 instead of bf16
   void* stream;
 };
 

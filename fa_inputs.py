@@ -7,7 +7,8 @@ does:
 * draws i.i.d. N(0,1) float32 values from one numpy PCG64 stream per
   (workload, tensor, batch, head), so any (b, h) slice can be regenerated on
   its own without materialising the whole tensor;
-* rounds float32 to bfloat16 bit patterns (round to nearest, ties to even);
+* rounds float32 to bfloat16 or IEEE fp16 bit patterns (round to nearest,
+  ties to even);
 * for the fp8 workload, injects x20 outliers with probability 1e-3 per element
   (each tensor has its own mask stream) and quantises to OCP FP8 E4M3FN codes
   with one float32 scale per 64 consecutive sequence rows of each (b, h),
@@ -136,6 +137,12 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return r
 
 
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest IEEE binary16, ties to even
+    (numpy's float32 -> float16 conversion); uint16 bits."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
 # ---------------------------------------------------------------------------
 # float -> OCP FP8 E4M3FN codes (bias 7, no infinities, 0x7F/0xFF are NaN)
 # ---------------------------------------------------------------------------
@@ -209,6 +216,19 @@ def bf16_tensor(wid: int, tensor_id: int, B: int, H: int, rows: int, d: int,
     def fill(bh):
         b, h = divmod(bh, H)
         out[b, h] = bf16_slice(wid, tensor_id, b, h, rows, d)
+
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(fill, range(B * H)))
+    return out
+
+
+def f16_tensor(wid: int, tensor_id: int, B: int, H: int, rows: int, d: int) -> np.ndarray:
+    """uint16 [B, H, rows, d] IEEE fp16 bits of the same normals as bf16_tensor."""
+    out = np.empty((B, H, rows, d), dtype=np.uint16)
+
+    def fill(bh):
+        b, h = divmod(bh, H)
+        out[b, h] = f32_to_f16_bits(normals(wid, tensor_id, b, h, rows, d))
 
     with ThreadPoolExecutor(_workers()) as ex:
         list(ex.map(fill, range(B * H)))

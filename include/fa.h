@@ -50,7 +50,8 @@ typedef enum {
 typedef enum {
   FA_BF16 = 0,
   FA_FP32 = 1,
-  FA_FP8_E4M3 = 2           /* OCP E4M3FN (bias 7, max 448), block-scaled */
+  FA_FP8_E4M3 = 2,          /* OCP E4M3FN (bias 7, max 448), block-scaled */
+  FA_FP16 = 3               /* IEEE binary16 */
 } fa_dtype;
 
 /*
@@ -86,7 +87,14 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  *                         rounded to E4M3FN for the P*V product; the row sum
  *                         uses the unrounded fp32 values.  d must be 128 and
  *                         out_dtype FA_BF16 (else FA_ERR_UNSUPPORTED).
- * out_dtype FA_BF16 or FA_FP32 (bf16 inputs) : o is [B,H,N,d] of that type.
+ * in_dtype  FA_FP16     : q, k, v IEEE fp16 [B,H,N,d] (the note's "使用注意事项"
+ *                         usage notes list FP16 beside BF16); the same
+ *                         kernel on the fp16 matrix cores, with P rounded
+ *                         to fp16 for the P*V product; d in {64, 128}; no
+ *                         scales.
+ * out_dtype FA_BF16 (bf16 inputs), FA_FP16 (fp16 inputs) or FA_FP32 (either):
+ *                         o is [B,H,N,d] of that type; any other pairing is
+ *                         FA_ERR_INVALID_ARG.
  * lse fp32 [B,H,N] (required).  stream is a hipStream_t (NULL = default).
  */
 typedef struct {

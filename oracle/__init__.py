@@ -7,7 +7,7 @@ generator (``fa_inputs``), which holds no attention arithmetic.
 
 Contents
 --------
-codecs      decode bf16 bit patterns and OCP E4M3FN codes to float64 from
+codecs      decode bf16 and IEEE fp16 bit patterns and OCP E4M3FN codes to float64 from
             their bit fields; dequantise 64-row block-scaled fp8 tensors.
 attention   the plain definition O = softmax(scale*Q*K^T)*V with its
             log-sum-exp, in float64, score matrix materialised, two passes
@@ -29,7 +29,7 @@ Every function is pinned by ``tests/test_oracle*.py`` against brute force,
 a library routine (torch's float64 scaled-dot-product attention on the CPU)
 and closed-form invariants.  Nothing in here is "parity unpinned".
 """
-from .codecs import decode_bf16, decode_e4m3fn, dequant_fp8_rows, round_to_e4m3fn  # noqa: F401
+from .codecs import decode_bf16, decode_e4m3fn, decode_f16, dequant_fp8_rows, round_to_e4m3fn  # noqa: F401
 from .attention import (  # noqa: F401
     attention, attention_rows, split_bounds, split_partials, merge_partials,
     decode_attention, decode_attention_gqa, fp8_p_error_bound, fp8_p_attention,

@@ -31,6 +31,26 @@ def decode_bf16(bits: np.ndarray) -> np.ndarray:
     return out
 
 
+def decode_f16(bits: np.ndarray) -> np.ndarray:
+    """IEEE binary16 bit patterns (uint16) -> float64.
+
+    1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.  Normal:
+    (-1)^s * 2^(E-15) * (1+F/1024); subnormal (E=0): (-1)^s * 2^-14 * F/1024;
+    E=31: inf (F=0) or NaN.
+    """
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    s = (b >> 15) & 1
+    E = (b >> 10) & 0x1F
+    F = b & 0x3FF
+    sign = np.where(s == 1, -1.0, 1.0)
+    normal = sign * np.ldexp(1.0 + F / 1024.0, (E - 15).astype(np.int32))
+    sub = sign * np.ldexp(F / 1024.0, -14)
+    out = np.where(E == 0, sub, normal)
+    out = np.where((E == 31) & (F == 0), sign * np.inf, out)
+    out = np.where((E == 31) & (F != 0), np.nan, out)
+    return out
+
+
 def decode_e4m3fn(codes: np.ndarray) -> np.ndarray:
     """OCP FP8 E4M3FN codes (uint8) -> float64.
 

@@ -17,6 +17,10 @@ def bf16_to_dev(bits: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
+def f16_to_dev(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.float16).cuda()
+
+
 def u8_to_dev(codes: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(codes)).cuda()
 
@@ -28,6 +32,8 @@ def dev_bf16_to_f64(t: torch.Tensor) -> np.ndarray:
 def dev_to_f64(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         return dev_bf16_to_f64(t)
+    if t.dtype == torch.float16:
+        return oracle.decode_f16(t.detach().cpu().view(torch.int16).numpy().view(np.uint16))
     return t.detach().cpu().numpy().astype(np.float64)
 
 

@@ -89,6 +89,17 @@ def test_fwd_ex_rejects(lib):
     p.out_dtype = fa.FA_FP32
     p.in_dtype = 7
     assert lib.fa_fwd_ex(ctypes.byref(p)) == fa.FA_ERR_INVALID_ARG
+    # 16-bit inputs write o in their own type or in fp32
+    p.in_dtype, p.out_dtype = fa.FA_BF16, fa.FA_FP16
+    assert lib.fa_fwd_ex(ctypes.byref(p)) == fa.FA_ERR_INVALID_ARG
+    p.in_dtype, p.out_dtype = fa.FA_FP16, fa.FA_BF16
+    assert lib.fa_fwd_ex(ctypes.byref(p)) == fa.FA_ERR_INVALID_ARG
+    p.out_dtype = fa.FA_FP16
+    p.d = 96
+    assert lib.fa_fwd_ex(ctypes.byref(p)) == fa.FA_ERR_UNSUPPORTED
+    p.d = 128
+    p.v_scale = A
+    assert lib.fa_fwd_ex(ctypes.byref(p)) == fa.FA_ERR_INVALID_ARG      # scales with fp16
 
 
 def test_workspace_bytes(lib):

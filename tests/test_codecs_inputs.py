@@ -4,7 +4,7 @@ import pytest
 import torch
 
 import fa_inputs as fi
-from oracle import decode_bf16, decode_e4m3fn, dequant_fp8_rows
+from oracle import decode_bf16, decode_e4m3fn, decode_f16, dequant_fp8_rows
 
 
 # ---------------------------------------------------------------------------
@@ -19,6 +19,31 @@ def test_bf16_decode_all_codes():
     nan = np.isnan(lib)
     assert np.array_equal(np.isnan(ours), nan)
     np.testing.assert_array_equal(ours[~nan], lib[~nan])
+
+
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")
+def test_f16_decode_all_codes():
+    codes = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ours = decode_f16(codes)
+    lib = codes.view(np.float16).astype(np.float64)
+    nan = np.isnan(lib)
+    assert nan.sum() == 2 * 1023
+    assert np.array_equal(np.isnan(ours), nan)
+    np.testing.assert_array_equal(ours[~nan], lib[~nan])
+    assert ours[0x3C00] == 1.0 and ours[0x7BFF] == 65504.0 and ours[0x0001] == 2.0 ** -24
+    assert ours[0x0400] == 2.0 ** -14 and ours[0xC000] == -2.0 and ours[0x7C00] == np.inf
+
+
+def test_f16_encode_matches_torch():
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32),
+                        np.float32([0.0, -0.0, 65504.0, 65520.0, 1e-8, 2.0 ** -25, 3 * 2.0 ** -25,
+                                    1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11])])
+    ours = fi.f32_to_f16_bits(x)
+    ref = torch.from_numpy(x).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+    # ties to even: 1 + 2^-11 lies halfway between 1 and 1 + 2^-10
+    assert ours[-2] == 0x3C00 and ours[-1] == 0x3C02 and ours[-6] == 0x7C00
 
 
 def test_e4m3fn_decode_all_codes():
