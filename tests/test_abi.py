@@ -18,7 +18,8 @@ def lib():
 
 
 def declared_functions():
-    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    with open(os.path.join(ROOT, "include", "fa.h")) as f:
+        text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(fa_\w+)\s*\(", text)))
 

@@ -34,6 +34,7 @@ def test_f16_decode_all_codes():
     assert ours[0x0400] == 2.0 ** -14 and ours[0xC000] == -2.0 and ours[0x7C00] == np.inf
 
 
+@pytest.mark.filterwarnings("ignore:overflow encountered in cast:RuntimeWarning")
 def test_f16_encode_matches_torch():
     rng = np.random.default_rng(1)
     x = np.concatenate([rng.standard_normal(100000).astype(np.float32),

@@ -28,7 +28,12 @@ def _rand(rng, *shape):
 # hand-worked cases
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("case", json.load(open(GOLDEN))["cases"], ids=lambda c: c["name"])
+def _golden_cases():
+    with open(GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
 def test_hand_worked(case):
     q, k, v = (np.array(case[n], dtype=np.float64) for n in ("q", "k", "v"))
     O, L = attention(q, k, v, case["scale"], case["causal"])
