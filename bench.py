@@ -56,19 +56,19 @@ COUNTER_SCALE = {"fetch": 1048576.0 / 524300.0, "write": 1.0}
 TRAFFIC_KIB = {
     "c3": {"src": ["fa_fwd_bf16.hip"], "fetch_kib": (257391.0 + 247438.0 + 264977.0) / 3,
            "write_kib": 66560.0,
-           "sha256": "e763869c6944be397367e44a7ad0863455ce8d2d3ebed206139fc62bb6a99d6b"},
+           "sha256": "cc06af71e9a86c3cea99062026fbc18bfeb878800eec78a92d7d5ec88e631725"},
     "c4": {"src": ["fa_decode.hip"],
            "fetch_kib": (4194784.0 + 4194625.0 + 4194618.0) / 3 + 4180.0,
            "write_kib": (8706.0 + 8707.0 + 8705.0) / 3 + 72.0,
-           "sha256": "68354608e0cfa829b4d3586aec42625d81df5ad26ffc40923d1d4ff0a0423f73"},
+           "sha256": "187fd05543296a83d140f0a11f7137c57d3ce55b56990ef77a7e9a2a10d0aa26"},
     "c6": {"src": ["fa_decode_gqa.hip", "fa_decode.hip"],
            "fetch_kib": (1085756.0 + 1086890.0 + 1087423.0) / 3 + (8342.0 + 8340.0 + 8340.0) / 3,
            "write_kib": (17408.0 + 17411.0 + 17411.0) / 3 + 144.0,
-           "sha256": "5db09feb3690d30c67d7521a98a025ef0093a915e2042f2be6961e33cf87e22e"},
+           "sha256": "cd7e9e57ac82ef64dc210b054d35238c404b389cf1db671cf7b6de1ec9215ba5"},
     "c7": {"src": ["fa_decode_gqa.hip", "fa_decode.hip"],
            "fetch_kib": (132958.0 + 132912.0 + 133009.0) / 3 + (4182.0 + 4180.0 + 4180.0) / 3,
            "write_kib": 8704.0 + 72.0,
-           "sha256": "5db09feb3690d30c67d7521a98a025ef0093a915e2042f2be6961e33cf87e22e"},
+           "sha256": "cd7e9e57ac82ef64dc210b054d35238c404b389cf1db671cf7b6de1ec9215ba5"},
 }
 
 

@@ -18,7 +18,7 @@ FA_BF16, FA_FP32, FA_FP8_E4M3, FA_FP16 = range(4)
 EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_decode_splitkv", "fa_decode_workspace_bytes",
            "fa_decode_splitkv_ex", "fa_decode_splitkv_gqa", "fa_decode_splitkv_varlen",
            "fa_fwd_varlen", "fa_fp8_quantize",
-           "fa_bwd_workspace_bytes", "fa_bwd",
+           "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_ex",
            "fa_status_string", "fa_last_error")
 
 
@@ -73,6 +73,8 @@ def load(path: str | None = None):
     lib.fa_bwd_workspace_bytes.restype = Z
     lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, Z, P]
     lib.fa_bwd.restype = I
+    lib.fa_bwd_ex.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, I, P, Z, P]
+    lib.fa_bwd_ex.restype = I
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
@@ -163,6 +165,15 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, workspa
     _check(load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                          _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
                          _ptr(workspace), int(workspace_bytes), _stream(stream)), "fa_bwd")
+
+
+def fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype=FA_BF16,
+              workspace=None, workspace_bytes=0, stream=None):
+    """fa_bwd with the tensor type as an argument: FA_BF16 or FA_FP16."""
+    _check(load().fa_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                            _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
+                            int(dtype), _ptr(workspace), int(workspace_bytes), _stream(stream)),
+           "fa_bwd_ex")
 
 
 def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, max_seqlen_q, max_seqlen_k,

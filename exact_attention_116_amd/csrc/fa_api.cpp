@@ -341,9 +341,12 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N) {
   return (n + 255u) & ~(size_t)255u;
 }
 
-fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                 const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
-                 float scale, int causal, void* workspace, size_t workspace_bytes, void* stream) {
+fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                    float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (dtype != FA_BF16 && dtype != FA_FP16)
+    return fail(FA_ERR_INVALID_ARG, "dtype must be FA_BF16 or FA_FP16");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
       !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return fail(FA_ERR_INVALID_ARG,
@@ -374,11 +377,19 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * kLog2e);
   a.causal = causal ? 1 : 0;
+  a.in_f16 = dtype == FA_FP16;
   a.stream = stream;
   hipError_t e = fa::launch_bwd(a);
   if (e != hipSuccess) return hip_fail(e, "fa_bwd launch");
   g_last_error.clear();
   return FA_OK;
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                 float scale, int causal, void* workspace, size_t workspace_bytes, void* stream) {
+  return fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, FA_BF16, workspace,
+                   workspace_bytes, stream);
 }
 
 const char* fa_status_string(fa_status s) {

@@ -13,6 +13,9 @@
 // (D equals rowsum(P * dP), the softmax Jacobian's correction term, because
 // O = P V.)
 //
+// IEEE fp16 tensors (F16) take the same kernels with the fp16 MFMA and fp16
+// roundings of P and dS; the statistics stay fp32.
+//
 // Three kernels, none of which needs atomics (so the result is
 // deterministic):
 //  1. fa_bwd_pre_kernel: D per query row, fp32, from bf16 O and dO.
@@ -123,7 +126,7 @@ struct TileReads {
 // ---------------------------------------------------------------------------
 // 1. D = rowsum(dO * O)
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool F16>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void fa_bwd_pre_kernel(const bf16* __restrict__ o, const bf16* __restrict__ dout,
                        float* __restrict__ dsum, long long rows) {
@@ -135,7 +138,7 @@ void fa_bwd_pre_kernel(const bf16* __restrict__ o, const bf16* __restrict__ dout
     const u32x4 a = *reinterpret_cast<const u32x4*>(o + row * D + 8 * part);
     const u32x4 b = *reinterpret_cast<const u32x4*>(dout + row * D + 8 * part);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) acc = dot2_bf16(a[w], b[w], acc);
+    for (int w = 0; w < 4; ++w) acc = dot2_16<F16>(a[w], b[w], acc);
   }
   acc = group_sum<LPR>(acc);
   if (row < rows && part == 0) dsum[row] = acc;
@@ -168,7 +171,7 @@ __device__ __forceinline__ void lds_barrier() {
 // the lower-numbered (older) role-0 waves win the issue arbitration, which
 // is the order the hand-off needs.  Q and dO rows are read row-wise for the
 // first product and through ds_read_b64_tr_b16 for the second.
-template <int D, int BQ, bool CAUSAL, int PD = 4>
+template <int D, int BQ, bool CAUSAL, bool F16, int PD = 4>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512)))
 void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                              const bf16* __restrict__ v, const bf16* __restrict__ dout,
@@ -280,7 +283,7 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
           for (int i = 0; i < NF + PD; ++i) {
             if (i < NF) f[i] = rd.rowfrag(A1, 32 * blk, i);
-            if (i >= PD) s = mfma32x32x16(f[i - PD], kv[i - PD], s);
+            if (i >= PD) s = mma16<F16>(f[i - PD], kv[i - PD], s);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -298,7 +301,7 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
               if (qi >= N || (CAUSAL && my_key > qi)) p0 = 0.f;
               if (qi + 1 >= N || (CAUSAL && my_key > qi + 1)) p1 = 0.f;
             }
-            pw[h] = pack_bf16(p0, p1);
+            pw[h] = pack16<F16>(p0, p1);
           }
           *reinterpret_cast<u32x4*>(pb + 16 * lane) = u32x4{pw[0], pw[1], pw[2], pw[3]};
           *reinterpret_cast<u32x4*>(pb + 1024 + 16 * lane) = u32x4{pw[4], pw[5], pw[6], pw[7]};
@@ -319,8 +322,8 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           for (int h = 0; h < 8; ++h) {
             const int i = 2 * h;
             const uint32_t w = h < 4 ? lo[h] : hi[h - 4];
-            const float p0 = bf16lo(w), p1 = bf16hi(w);
-            sw[h] = pack_bf16(p0 * (s[i] - x4[i >> 2][i & 3]),
+            const float p0 = lo16<F16>(w), p1 = hi16<F16>(w);
+            sw[h] = pack16<F16>(p0 * (s[i] - x4[i >> 2][i & 3]),
                               p1 * (s[i + 1] - x4[i >> 2][(i & 3) + 1]));
           }
           bo[0] = __builtin_bit_cast(bf16x8, u32x4{sw[0], sw[1], sw[2], sw[3]});
@@ -333,7 +336,7 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           if (i < NF) f[i] = rd.trfrag(A2, 32 * blk + 16 * (i / NC), i % NC);
           if (i >= PD) {
             const int x = i - PD;
-            acc[x % NC] = mfma32x32x16(f[x], bo[x / NC], acc[x % NC]);
+            acc[x % NC] = mma16<F16>(f[x], bo[x / NC], acc[x % NC]);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -354,8 +357,8 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       for (int ii = 0; ii < 4; ++ii) {
         const int d0 = 32 * cb + 8 * ii + 4 * g;
         *reinterpret_cast<u32x2*>(out + d0) =
-            u32x2{pack_bf16(m * acc[cb][4 * ii], m * acc[cb][4 * ii + 1]),
-                  pack_bf16(m * acc[cb][4 * ii + 2], m * acc[cb][4 * ii + 3])};
+            u32x2{pack16<F16>(m * acc[cb][4 * ii], m * acc[cb][4 * ii + 1]),
+                  pack16<F16>(m * acc[cb][4 * ii + 2], m * acc[cb][4 * ii + 3])};
       }
   }
 }
@@ -363,7 +366,7 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 // ---------------------------------------------------------------------------
 // 3. dQ: query tiles outer
 // ---------------------------------------------------------------------------
-template <int D, int BC, int NW, bool CAUSAL>
+template <int D, int BC, int NW, bool CAUSAL, bool F16>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                       const bf16* __restrict__ v, const bf16* __restrict__ dout,
@@ -452,8 +455,8 @@ void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           if (i < NF) f[i] = rd.rowfrag((i & 1) ? Vs : Ks, 32 * blk, i >> 1);
           if (i >= PD) {
             const int x = i - PD;
-            if (x & 1) dp = mfma32x32x16(f[x], ob[x >> 1], dp);
-            else s = mfma32x32x16(f[x], qb[x >> 1], s);
+            if (x & 1) dp = mma16<F16>(f[x], ob[x >> 1], dp);
+            else s = mma16<F16>(f[x], qb[x >> 1], s);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -477,7 +480,7 @@ void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
             }
             dsv[e] = p * (dp[i] - dd);
           }
-          w[h] = pack_bf16(dsv[0], dsv[1]);
+          w[h] = pack16<F16>(dsv[0], dsv[1]);
         }
         ps[t] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
       }
@@ -490,7 +493,7 @@ void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           if (i < NF) f[i] = rd.trfrag(Ks, 32 * blk + 16 * (i / NC), i % NC);
           if (i >= PD) {
             const int x = i - PD;
-            acc[x % NC] = mfma32x32x16(f[x], ps[x / NC], acc[x % NC]);
+            acc[x % NC] = mma16<F16>(f[x], ps[x / NC], acc[x % NC]);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -509,14 +512,14 @@ void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       for (int ii = 0; ii < 4; ++ii) {
         const int d0 = 32 * cb + 8 * ii + 4 * g;
         *reinterpret_cast<u32x2*>(dq + row * D + d0) =
-            u32x2{pack_bf16(scale * acc[cb][4 * ii], scale * acc[cb][4 * ii + 1]),
-                  pack_bf16(scale * acc[cb][4 * ii + 2], scale * acc[cb][4 * ii + 3])};
+            u32x2{pack16<F16>(scale * acc[cb][4 * ii], scale * acc[cb][4 * ii + 1]),
+                  pack16<F16>(scale * acc[cb][4 * ii + 2], scale * acc[cb][4 * ii + 3])};
       }
   }
 }
 
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F16>
 static hipError_t launch_bwd_d(const BwdArgs& a) {
   // dK/dV: 128 keys per workgroup (four wave pairs, two waves per SIMD),
   // 128-query tiles (against 64: +3% at N = 16384, causal).
@@ -527,28 +530,33 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
   const int BH = a.B * a.H;
   hipStream_t st = (hipStream_t)a.stream;
   const long long rows = (long long)BH * a.N;
-  hipLaunchKernelGGL((fa_bwd_pre_kernel<D>), dim3((unsigned)((rows + (256 / (D / 8)) - 1) / (256 / (D / 8)))),
+  hipLaunchKernelGGL((fa_bwd_pre_kernel<D, F16>), dim3((unsigned)((rows + (256 / (D / 8)) - 1) / (256 / (D / 8)))),
                      dim3(256), 0, st, (const bf16*)a.o, (const bf16*)a.dout, a.dsum, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nkt = (a.N + BCK - 1) / BCK;
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BQ, CAUSAL>), dim3((unsigned)((long long)nkt * BH)),
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BQ, CAUSAL, F16>), dim3((unsigned)((long long)nkt * BH)),
                      dim3(NWK * 64), 0, st, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
                      (const bf16*)a.dout, a.lse, a.dsum, (bf16*)a.dk, (bf16*)a.dv, BH, a.N,
                      a.scale_log2, a.scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nqt = (a.N + NWQ * 32 - 1) / (NWQ * 32);
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BCQ, NWQ, CAUSAL>), dim3((unsigned)((long long)nqt * BH)),
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BCQ, NWQ, CAUSAL, F16>), dim3((unsigned)((long long)nqt * BH)),
                      dim3(NWQ * 64), 0, st, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
                      (const bf16*)a.dout, a.lse, a.dsum, (bf16*)a.dq, BH, a.N, a.scale_log2,
                      a.scale);
   return hipGetLastError();
 }
 
+template <bool F16>
+static hipError_t launch_bwd_t(const BwdArgs& a) {
+  if (a.d == 128) return a.causal ? launch_bwd_d<128, true, F16>(a) : launch_bwd_d<128, false, F16>(a);
+  return a.causal ? launch_bwd_d<64, true, F16>(a) : launch_bwd_d<64, false, F16>(a);
+}
+
 hipError_t launch_bwd(const BwdArgs& a) {
-  if (a.d == 128) return a.causal ? launch_bwd_d<128, true>(a) : launch_bwd_d<128, false>(a);
-  return a.causal ? launch_bwd_d<64, true>(a) : launch_bwd_d<64, false>(a);
+  return a.in_f16 ? launch_bwd_t<true>(a) : launch_bwd_t<false>(a);
 }
 
 }  // namespace fa

@@ -105,6 +105,13 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
 __device__ __forceinline__ float bf16lo(uint32_t w) { return as_f32(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return as_f32(w & 0xFFFF0000u); }
 
+// The same for fp16 pairs.
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc, false);
+}
+__device__ __forceinline__ float f16lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[0]; }
+__device__ __forceinline__ float f16hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[1]; }
+
 // Buffer resource over [base, base + bytes): loads past the end return 0,
 // which is how the kernels read tiles that overhang the sequence without a
 // branch.  Offsets are 32-bit byte offsets from base.
@@ -147,6 +154,21 @@ template <bool F16>
 __device__ __forceinline__ uint32_t pack16(float a, float b) {
   if constexpr (F16) return pack_f16(a, b);
   else return pack_bf16(a, b);
+}
+template <bool F16>
+__device__ __forceinline__ float lo16(uint32_t w) {
+  if constexpr (F16) return f16lo(w);
+  else return bf16lo(w);
+}
+template <bool F16>
+__device__ __forceinline__ float hi16(uint32_t w) {
+  if constexpr (F16) return f16hi(w);
+  else return bf16hi(w);
+}
+template <bool F16>
+__device__ __forceinline__ float dot2_16(uint32_t a, uint32_t b, float acc) {
+  if constexpr (F16) return dot2_f16(a, b, acc);
+  else return dot2_bf16(a, b, acc);
 }
 
 }  // namespace fa

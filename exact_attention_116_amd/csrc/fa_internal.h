@@ -63,6 +63,7 @@ struct BwdArgs {
   float scale;
   float scale_log2;
   int causal;
+  int in_f16;         // fp16 tensors instead of bf16
   void* stream;
 };
 

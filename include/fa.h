@@ -273,6 +273,21 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  float scale, int causal, void* workspace, size_t workspace_bytes,
                  void* stream);
 
+/*
+ * fa_bwd_ex -- fa_bwd with the tensor type as an argument: dtype FA_BF16
+ * (exactly fa_bwd) or FA_FP16, for the mixed-precision training of the Flash
+ * Attention note's "使用注意事项" usage notes (an fp16 forward pass, fp32
+ * softmax statistics in the backward pass).  With FA_FP16, q, k, v, o, dout,
+ * dq, dk and dv are IEEE fp16 [B, H, N, d] (o and lse from fa_fwd_ex with
+ * in_dtype = out_dtype = FA_FP16); P and dS are rounded to fp16 for the
+ * matrix cores, D and the accumulation stay fp32.  Any other dtype is
+ * FA_ERR_INVALID_ARG.  Everything else is as for fa_bwd.
+ */
+fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                    float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
 /* A static string naming the status. */
 const char* fa_status_string(fa_status s);
 

@@ -218,6 +218,36 @@ def test_decode_varlen_rejects(lib, kw, status):
     assert st == status
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dq=A + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=None), fa.FA_ERR_INVALID_ARG),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=1 << 24), fa.FA_ERR_UNSUPPORTED),       # a 4 GiB head: beyond 32-bit offsets
+    (dict(ws=A, ws_bytes=64), fa.FA_ERR_WORKSPACE),   # smaller than fa_bwd_workspace_bytes
+    (dict(ws=None, ws_bytes=64), fa.FA_ERR_WORKSPACE),
+    (dict(ws=A + 8, ws_bytes=1 << 20), fa.FA_ERR_WORKSPACE),
+    (dict(dtype=fa.FA_FP32), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=fa.FA_FP8_E4M3), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=7), fa.FA_ERR_INVALID_ARG),
+])
+def test_bwd_rejects(lib, kw, status):
+    a = dict(q=A, k=A, v=A, o=A, do=A, lse=A, dq=A, dk=A, dv=A, B=1, H=2, N=100, d=128, scale=0.1,
+             causal=1, dtype=fa.FA_BF16, ws=A, ws_bytes=1 << 20)
+    a.update(kw)
+    args = [a[x] for x in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "B", "H", "N", "d",
+                           "scale", "causal")]
+    st = lib.fa_bwd_ex(*args, a["dtype"], a["ws"], a["ws_bytes"], None)
+    assert st == status
+    assert fa.fa_last_error() != ""
+    if a["dtype"] == fa.FA_BF16:      # fa_bwd is fa_bwd_ex with FA_BF16
+        assert lib.fa_bwd(*args, a["ws"], a["ws_bytes"], None) == status
+    assert fa.fa_bwd_workspace_bytes(1, 2, 100) == 1024   # 800 rounded up to 256
+
+
 def test_binding_raises_with_status():
     with pytest.raises(fa.FaError) as e:
         fa.fa_fwd(A, A, A, A, None, 1, 1, 16, 128, 0.1, False)
