@@ -84,11 +84,18 @@ def load(path: str | None = None):
 
 
 def _ptr(x):
-    """Device address of a tensor (``data_ptr()``), an int, or None."""
+    """Device address of a tensor (``data_ptr()``), an int (taken as a device
+    address as is), or None.  A tensor must live on a GPU and be contiguous:
+    the kernels read the dense layouts ``include/fa.h`` states, and a host
+    address handed to a kernel would fault the device."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
+    if not getattr(x, "is_cuda", False):
+        raise FaError(FA_ERR_INVALID_ARG, "tensor arguments must be GPU tensors")
+    if not x.is_contiguous():
+        raise FaError(FA_ERR_INVALID_ARG, "tensor arguments must be contiguous")
     return x.data_ptr()
 
 

@@ -170,7 +170,7 @@ fa_status owned_workspace(size_t need, void** out) {
     e = hipMalloc(&g_ws.ptr[dev], need);
     if (e != hipSuccess) {
       g_ws.ptr[dev] = nullptr;
-      return fail(FA_ERR_WORKSPACE, "could not allocate the decode workspace");
+      return fail(FA_ERR_WORKSPACE, "could not allocate the library-owned workspace");
     }
     g_ws.bytes[dev] = need;
   }

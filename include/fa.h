@@ -27,8 +27,11 @@
  *     returns FA_ERR_HIP (fa_last_error() has the HIP text); faults inside a
  *     kernel surface at the caller's next synchronisation.
  *   - Calls that share a library-owned workspace (fa_decode_splitkv, and
- *     fa_decode_splitkv_gqa or fa_bwd with a NULL workspace) on one device
- *     must not run concurrently on different streams.
+ *     fa_decode_splitkv_gqa, fa_decode_splitkv_varlen, fa_bwd or fa_bwd_ex
+ *     with a NULL workspace) on one device must not run concurrently on
+ *     different streams.  Growing that workspace synchronises the device
+ *     (hipDeviceSynchronize), so such calls are not for graph capture; pass
+ *     a workspace there.
  */
 #ifndef FA_H_
 #define FA_H_

@@ -248,6 +248,26 @@ def test_bwd_rejects(lib, kw, status):
     assert fa.fa_bwd_workspace_bytes(1, 2, 100) == 1024   # 800 rounded up to 256
 
 
+def test_binding_rejects_host_and_strided_tensors():
+    import torch
+    x = torch.zeros(1, 1, 16, 128, dtype=torch.bfloat16)
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_fwd(x, x, x, x, x, 1, 1, 16, 128, 0.1, False)
+    assert e.value.status == fa.FA_ERR_INVALID_ARG and "GPU" in str(e.value)
+
+    class FakeDevice:   # a GPU tensor stand-in that is not contiguous
+        is_cuda = True
+
+        def is_contiguous(self):
+            return False
+
+        def data_ptr(self):
+            return A
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_fwd(FakeDevice(), A, A, A, A, 1, 1, 16, 128, 0.1, False)
+    assert "contiguous" in str(e.value)
+
+
 def test_binding_raises_with_status():
     with pytest.raises(fa.FaError) as e:
         fa.fa_fwd(A, A, A, A, None, 1, 1, 16, 128, 0.1, False)
