@@ -148,12 +148,15 @@ struct OwnedWorkspace {
 };
 OwnedWorkspace g_ws;
 
-// The current device's library-owned workspace, at least `need` bytes.
-fa_status owned_workspace(size_t need, void** out) {
+// The current device's library-owned workspace, at least `need` bytes.  On
+// success `lock` holds the workspace mutex; the caller keeps it until the
+// launch that uses the buffer is queued, so that no other thread can grow
+// (free and reallocate) the buffer in between.
+fa_status owned_workspace(size_t need, void** out, std::unique_lock<std::mutex>& lock) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  std::lock_guard<std::mutex> lock(g_ws.mu);
+  lock = std::unique_lock<std::mutex>(g_ws.mu);
   if ((int)g_ws.ptr.size() <= dev) {
     g_ws.ptr.resize(dev + 1, nullptr);
     g_ws.bytes.resize(dev + 1, 0);
@@ -192,9 +195,10 @@ fa_status decode_grouped(const void* q, const void* kcache, const void* vcache, 
     return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
   const size_t need = decode_ws_bytes(B, Hq, d, num_splits);
   void* ws = workspace;
+  std::unique_lock<std::mutex> ws_lock;   // held through the launch when ws is library-owned
   if (!workspace) {
     if (workspace_bytes != 0) return fail(FA_ERR_WORKSPACE, "workspace is NULL but workspace_bytes is not 0");
-    st = owned_workspace(need, &ws);
+    st = owned_workspace(need, &ws, ws_lock);
     if (st != FA_OK) return st;
   } else {
     if (!aligned16(workspace)) return fail(FA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
@@ -249,7 +253,8 @@ fa_status fa_decode_splitkv(const void* q, const void* kcache, const void* vcach
   fa_status st = check_decode(q, kcache, vcache, o, B, H, Lkv, d, num_splits, scale);
   if (st != FA_OK) return st;
   void* ws = nullptr;
-  st = owned_workspace(decode_ws_bytes(B, H, d, num_splits), &ws);
+  std::unique_lock<std::mutex> ws_lock;   // held through the launch
+  st = owned_workspace(decode_ws_bytes(B, H, d, num_splits), &ws, ws_lock);
   if (st != FA_OK) return st;
   return run_decode(q, kcache, vcache, o, nullptr, B, H, 0, Lkv, d, num_splits, scale, ws, nullptr);
 }
@@ -361,9 +366,10 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
     return fail(FA_ERR_UNSUPPORTED, "one (batch, head) slice must be smaller than 4 GiB");
   const size_t need = fa_bwd_workspace_bytes(B, H, N);
   void* ws = workspace;
+  std::unique_lock<std::mutex> ws_lock;   // held through the launch when ws is library-owned
   if (!workspace) {
     if (workspace_bytes != 0) return fail(FA_ERR_WORKSPACE, "workspace is NULL but workspace_bytes is not 0");
-    fa_status st = owned_workspace(need, &ws);
+    fa_status st = owned_workspace(need, &ws, ws_lock);
     if (st != FA_OK) return st;
   } else {
     if (!aligned16(workspace)) return fail(FA_ERR_WORKSPACE, "workspace must be 16-byte aligned");

@@ -29,9 +29,12 @@
  *   - Calls that share a library-owned workspace (fa_decode_splitkv, and
  *     fa_decode_splitkv_gqa, fa_decode_splitkv_varlen, fa_bwd or fa_bwd_ex
  *     with a NULL workspace) on one device must not run concurrently on
- *     different streams.  Growing that workspace synchronises the device
- *     (hipDeviceSynchronize), so such calls are not for graph capture; pass
- *     a workspace there.
+ *     different streams.  From several host threads on one stream they are
+ *     safe: each call queues all of its launches while holding the
+ *     workspace lock, so the buffer is neither freed nor shared between
+ *     the launches of one call.  Growing that workspace synchronises the
+ *     device (hipDeviceSynchronize), so such calls are not for graph
+ *     capture; pass a workspace there.
  */
 #ifndef FA_H_
 #define FA_H_

@@ -118,3 +118,51 @@ def test_decode_deterministic_and_in_bounds(gpu_lib):
     assert torch.equal(outs[0][1], outs[1][1])
     for buf, n in ((obuf, nel), (lbuf, B * H), (wbuf, need // 4)):
         assert torch.all(buf[:G] == 7.0) and torch.all(buf[G + n:] == 7.0)
+
+
+def test_decode_owned_workspace_from_two_threads(gpu_lib):
+    """Two host threads share the library-owned workspace on one stream while
+    it grows: each call queues its split and merge launches under the
+    workspace lock, so no call reads a freed buffer or another call's
+    partials.  Every output meets the gates and equals the other calls of
+    its size bit for bit."""
+    import threading
+    fa = gpu_lib
+    d, Lkv, S, H = 64, 64, 64, 16
+    sizes = [32, 64, 128]       # B: workspace of 8.5, 17 and 34 MB
+    rounds = 3
+    say(f"decode from two threads, library-owned workspace, B in {sizes}, H={H} Lkv={Lkv} d={d} splits={S}")
+    data, refs = {}, {}
+    for B in sizes:
+        qb, kb, vb = gen(4700 + B, B, H, Lkv, d)
+        data[B] = tuple(map(bf16_to_dev, (qb, kb, vb)))
+        refs[B] = oracle.decode_attention(*map(oracle.decode_bf16, (qb, kb, vb)), d ** -0.5)[0]
+    outs = {(t, r, B): torch.empty((B, H, 1, d), dtype=torch.bfloat16, device="cuda")
+            for t in range(2) for r in range(rounds) for B in sizes}
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(t):
+        try:
+            order = sizes if t == 0 else sizes[::-1]
+            for r in range(rounds):
+                for B in order:
+                    q, k, v = data[B]
+                    fa.fa_decode_splitkv(q, k, v, outs[(t, r, B)], B, H, Lkv, d, S)
+        except Exception as e:  # noqa: BLE001 - reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for B in sizes:
+        first = outs[(0, 0, B)]
+        for key, o in outs.items():
+            if key[2] == B:
+                assert torch.equal(o, first), key
+        err = np.abs(dev_to_f64(first) - refs[B])
+        assert err.max() <= 1e-2 and err.mean() <= 1e-3, (B, err.max(), err.mean())
