@@ -52,22 +52,38 @@ def bf16_floor(o_ref):
     return np.abs(oracle.decode_bf16(fa_inputs.f32_to_bf16_bits(o_ref.astype(np.float32))) - o_ref)
 
 
-def check_bf16_gates(o_got, o_ref, lse_got, lse_ref, what="", beyond_floor=False):
+def half_ulp(x, mant_bits=8):
+    """Half the spacing of a binary format with mant_bits significant bits
+    (bf16: 8, fp16: 11) at |x|: the most that rounding a value to it moves it."""
+    a = np.maximum(np.abs(np.asarray(x, np.float64)), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(a)) - mant_bits)
+
+
+def check_bf16_gates(o_got, o_ref, lse_got, lse_ref, what="", beyond_floor=False, mant_bits=8):
     """max-abs <= 1e-2, mean-abs <= 1e-3, LSE relative <= 1e-3.
 
     beyond_floor: for shapes outside the measured workloads, where a row mixes
-    only a few values and |O| ~ 1, merely storing the exact O as bf16 already
-    costs a mean error near 1e-3; the mean gate then applies to the error
-    beyond that floor (mean-abs <= 1e-3 + mean |bf16(O) - O|).
+    only a few values and |O| ~ 1 or more.  Merely storing the exact O as bf16
+    already costs a mean error near 1e-3 there, so the mean gate applies to
+    the error beyond that floor (mean-abs <= 1e-3 + mean |bf16(O) - O|).  Once
+    |O| passes 2 (nearly one-hot rows of N(0,1) values) one bf16 step is
+    1.6e-2, more than the max gate, so the max gate applies to the kernel's
+    result before its final rounding: |O_out - O| <= 1e-2 + half a step of
+    the output type (mant_bits significant bits) at max(|O|, |O_out|).
     """
-    err = np.abs(np.asarray(o_got, np.float64) - o_ref)
+    o_got = np.asarray(o_got, np.float64)
+    err = np.abs(o_got - o_ref)
     assert np.all(np.isfinite(o_got)), f"{what}: non-finite output"
     mx, mean = float(err.max()), float(err.mean())
     lr = float(lse_rel(lse_got, lse_ref).max())
     fl = bf16_floor(o_ref)
     print(f"  {what}: max_abs={mx:.3e} mean_abs={mean:.3e} lse_rel={lr:.3e} "
           f"(bf16 floor max={fl.max():.3e} mean={fl.mean():.3e})", flush=True)
-    assert mx <= MAX_ABS, f"{what}: max-abs {mx}"
+    if beyond_floor:
+        excess = float((err - half_ulp(np.maximum(np.abs(o_ref), np.abs(o_got)), mant_bits)).max())
+        assert excess <= MAX_ABS, f"{what}: max-abs beyond the output rounding {excess}"
+    else:
+        assert mx <= MAX_ABS, f"{what}: max-abs {mx}"
     mean_gate = MEAN_ABS + (float(fl.mean()) if beyond_floor else 0.0)
     assert mean <= mean_gate, f"{what}: mean-abs {mean} > {mean_gate}"
     assert lr <= LSE_REL, f"{what}: LSE relative {lr}"

@@ -123,3 +123,48 @@ def test_large_scores_stay_finite(gpu_lib):
         o, lse = run_fwd(fa, *map(bf16_to_dev, (qb, kb, vb)), B, H, N, d, d ** -0.5, causal)
         O, L = oracle.attention(*map(oracle.decode_bf16, (qb, kb, vb)), d ** -0.5, causal)
         check_bf16_gates(dev_to_f64(o), O, dev_to_f64(lse), L, f"x100 causal={causal}")
+
+
+def ramped_inputs(wid, H, N, d, ramp):
+    """N(0,1) q, k, v with the key rows scaled by 2^(j/256) ("up") or by its
+    mirror ("down"): the scaled scores' spread doubles every 256 keys (or
+    halves), so along "up" the running row max grows by more than 2^8 (in
+    base-2 units) across many key tiles, and along "down" every later tile
+    is dwarfed by the first."""
+    x = [np.stack([fi.normals(wid, t, 0, h, N, d) for h in range(H)])[None] for t in range(3)]
+    f = (2.0 ** (np.arange(N) / 256.0)).astype(np.float32)
+    if ramp == "down":
+        f = f[::-1].copy()
+    x[1] = x[1] * f[None, None, :, None]
+    return [fi.f32_to_bf16_bits(a.astype(np.float32)) for a in x]
+
+
+@pytest.mark.parametrize("ramp", ["up", "down"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_growing_and_shrinking_scores(gpu_lib, ramp, causal):
+    """The lazy rescale taken in many key tiles (keys of growing norm), and
+    probabilities that underflow after the first tile (shrinking norm)."""
+    fa = gpu_lib
+    B, H, N, d = 1, 2, 1024, 128
+    say(f"fwd ramped key norms ({ramp}) causal={causal} N={N}")
+    qb, kb, vb = ramped_inputs(3100 + (ramp == "down"), H, N, d, ramp)
+    o, lse = run_fwd(fa, *map(bf16_to_dev, (qb, kb, vb)), B, H, N, d, d ** -0.5, causal)
+    O, L = oracle.attention(*map(oracle.decode_bf16, (qb, kb, vb)), d ** -0.5, causal)
+    check_bf16_gates(dev_to_f64(o), O, dev_to_f64(lse), L, f"ramp {ramp} causal={causal}",
+                     beyond_floor=True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("scale", [1e-3, 0.05, 1.0, 2.5])
+def test_softmax_scale(gpu_lib, scale, d):
+    """Scales other than 1/sqrt(d), from nearly uniform weights (1e-3) to
+    nearly one-hot rows (2.5 with d = 128: scaled scores of spread ~28)."""
+    fa = gpu_lib
+    B, H, N = 1, 2, 300
+    say(f"fwd scale={scale} d={d} N={N}")
+    qb, kb, vb = gen(3200 + d, B, H, N, d)
+    for causal in (False, True):
+        o, lse = run_fwd(fa, *map(bf16_to_dev, (qb, kb, vb)), B, H, N, d, scale, causal)
+        O, L = oracle.attention(*map(oracle.decode_bf16, (qb, kb, vb)), scale, causal)
+        check_bf16_gates(dev_to_f64(o), O, dev_to_f64(lse), L, f"scale={scale} causal={causal}",
+                         beyond_floor=True)

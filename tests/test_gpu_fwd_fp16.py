@@ -90,3 +90,26 @@ def test_fp16_and_bf16_agree_on_common_values(gpu_lib):
     torch.cuda.synchronize()
     assert (o16.float() - ob.float()).abs().max().item() <= 2e-2
     assert (l16 - lb).abs().max().item() <= 1e-4
+
+
+@pytest.mark.parametrize("ramp", ["up", "down"])
+def test_fp16_growing_and_shrinking_scores(gpu_lib, ramp):
+    """fp16 inputs whose key norms double (or halve) every 256 keys: the lazy
+    rescale is taken in many key tiles, P is rounded to fp16 at values up to
+    2^8, and along "down" later probabilities fall below fp16's range in P*V
+    while still counting in the fp32 row sum."""
+    fa = gpu_lib
+    B, H, N, d = 1, 2, 1024, 128
+    say(f"fwd fp16 ramped key norms ({ramp}) causal N={N}")
+    x = [np.stack([fi.normals(5200 + (ramp == "down"), t, 0, h, N, d) for h in range(H)])[None]
+         for t in range(3)]
+    f = (2.0 ** (np.arange(N) / 256.0)).astype(np.float32)
+    if ramp == "down":
+        f = f[::-1].copy()
+    x[1] = x[1] * f[None, None, :, None]
+    qb, kb, vb = (fi.f32_to_f16_bits(a.astype(np.float32)) for a in x)
+    for causal in (False, True):
+        o, lse = run_fwd16(fa, *map(f16_to_dev, (qb, kb, vb)), B, H, N, d, d ** -0.5, causal)
+        O, L = oracle.attention(*map(oracle.decode_f16, (qb, kb, vb)), d ** -0.5, causal)
+        check_bf16_gates(dev_to_f64(o), O, dev_to_f64(lse), L, f"fp16 ramp {ramp} causal={causal}",
+                         beyond_floor=True, mant_bits=11)
