@@ -54,9 +54,9 @@ PEAK_HBM_GBS = 8000.0
 # split-merge kernel's counters to the split kernel's.
 COUNTER_SCALE = {"fetch": 1048576.0 / 524300.0, "write": 1.0}
 TRAFFIC_KIB = {
-    "c3": {"src": ["fa_fwd_bf16.hip"], "fetch_kib": (257391.0 + 247438.0 + 264977.0) / 3,
+    "c3": {"src": ["fa_fwd_bf16.hip"], "fetch_kib": (262080.3125 + 283009.9375 + 281869.125) / 3,
            "write_kib": 66560.0,
-           "sha256": "cc06af71e9a86c3cea99062026fbc18bfeb878800eec78a92d7d5ec88e631725"},
+           "sha256": "6d4e8e3753d4ebbb3c30cd503d69a7f789552180ce8b8d0050bc2dfbf6dfa972"},
     "c4": {"src": ["fa_decode.hip"],
            "fetch_kib": (4194784.0 + 4194625.0 + 4194618.0) / 3 + 4180.0,
            "write_kib": (8706.0 + 8707.0 + 8705.0) / 3 + 72.0,

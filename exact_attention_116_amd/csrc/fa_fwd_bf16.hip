@@ -89,7 +89,11 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * (C::KTILE + C::VTILE)];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  // the wave index as a uniform value, so that the LDS targets of the
+  // direct loads are computed in scalar registers (no per-load
+  // v_readfirstlane into M0)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
 
   const int bh = blockIdx.x % BH;

@@ -90,7 +90,8 @@ void fa_fwd_fp8_dl_kernel(const uint8_t* __restrict__ q, const uint8_t* __restri
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * TB];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS targets in SGPRs
   const int l32 = lane & 31, g = lane >> 5;
 
   const int nqt = (N + BRW - 1) / BRW;
