@@ -141,3 +141,37 @@ def test_bwd_deterministic_and_in_bounds(gpu_lib):
     for b in bufs:
         assert torch.all(b[:G] == 7.0) and torch.all(b[G + nel:] == 7.0)
     assert torch.all(wbuf[:G] == 7.0) and torch.all(wbuf[G + need // 4:] == 7.0)
+
+
+@pytest.mark.parametrize("ramp", ["up", "down"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_growing_and_shrinking_scores(gpu_lib, ramp, causal):
+    """Key norms that double (or halve) every 256 keys: the forward's lazy
+    rescale moves the reference max in many key tiles, and the backward
+    recomputes P from that pass's LSE over rows that are nearly one-hot."""
+    fa = gpu_lib
+    B, H, N, d = 1, 2, 1024, 128
+    say(f"bwd ramped key norms ({ramp}) causal={causal} N={N}")
+    x = [np.stack([fi.normals(7300 + (ramp == "down"), t, 0, h, N, d) for h in range(H)])[None]
+         for t in (fi.Q_ID, fi.K_ID, fi.V_ID, fi.DO_ID)]
+    f = (2.0 ** (np.arange(N) / 256.0)).astype(np.float32)
+    if ramp == "down":
+        f = f[::-1].copy()
+    x[1] = x[1] * f[None, None, :, None]
+    qb, kb, vb, dob = (fi.f32_to_bf16_bits(a.astype(np.float32)) for a in x)
+    got = run(fa, *map(bf16_to_dev, (qb, kb, vb, dob)), B, H, N, d, d ** -0.5, causal)
+    ref = oracle.attention_backward(*map(oracle.decode_bf16, (qb, kb, vb, dob)), d ** -0.5, causal)
+    check(got, ref, f"ramp {ramp} causal={causal}")
+
+
+@pytest.mark.parametrize("scale", [0.05, 1.0])
+def test_bwd_softmax_scale(gpu_lib, scale):
+    """Scales other than 1/sqrt(d): nearly uniform and nearly one-hot rows."""
+    fa = gpu_lib
+    B, H, N, d = 1, 2, 300, 64
+    say(f"bwd scale={scale} N={N} d={d}")
+    qb, kb, vb, dob = gen(7400, B, H, N, d)
+    for causal in (False, True):
+        got = run(fa, *map(bf16_to_dev, (qb, kb, vb, dob)), B, H, N, d, scale, causal)
+        ref = oracle.attention_backward(*map(oracle.decode_bf16, (qb, kb, vb, dob)), scale, causal)
+        check(got, ref, f"scale={scale} causal={causal}")

@@ -166,3 +166,31 @@ def test_decode_owned_workspace_from_two_threads(gpu_lib):
                 assert torch.equal(o, first), key
         err = np.abs(dev_to_f64(first) - refs[B])
         assert err.max() <= 1e-2 and err.mean() <= 1e-3, (B, err.max(), err.mean())
+
+
+@pytest.mark.parametrize("ramp", ["up", "down"])
+def test_decode_splits_of_very_different_weight(gpu_lib, ramp):
+    """Key norms that double (or halve) every 1024 keys of an 8192-key cache
+    cut into 64 splits: the splits' LSE differ by tens, so most merge weights
+    exp(LSE_s - LSE) underflow and one end of the cache decides the output."""
+    fa = gpu_lib
+    B, H, Lkv, d, S = 2, 4, 8192, 128, 64
+    say(f"decode ramped key norms ({ramp}) Lkv={Lkv} splits={S}")
+    qb = fi.bf16_tensor(4800, fi.Q_ID, B, H, 1, d)
+    k = np.stack([np.stack([fi.normals(4800 + (ramp == "down"), fi.K_ID, b, h, Lkv, d) for h in range(H)])
+                  for b in range(B)])
+    f = (2.0 ** (np.arange(Lkv) / 1024.0)).astype(np.float32)
+    if ramp == "down":
+        f = f[::-1].copy()
+    kb = fi.f32_to_bf16_bits(k * f[None, None, :, None])
+    vb = fi.bf16_tensor(4800, fi.V_ID, B, H, Lkv, d)
+    scale = d ** -0.5
+    o, lse, po, pl = run_ex(fa, *map(bf16_to_dev, (qb, kb, vb)), B, H, Lkv, d, S, scale)
+    q, kk, v = map(oracle.decode_bf16, (qb, kb, vb))
+    O, L = oracle.decode_attention(q, kk, v, scale)
+    check_bf16_gates(dev_to_f64(o)[:, :, 0], O[:, :, 0], dev_to_f64(lse), L[:, :, 0], f"ramp {ramp}",
+                     beyond_floor=True)
+    Ls = oracle.split_partials(q, kk, v, scale, S)[1][:, :, :, 0]
+    spread = float((Ls.max(-1) - Ls.min(-1)).min())
+    say(f"  smallest spread of split LSEs over (b, h): {spread:.1f}")
+    assert spread > 20.0   # the case really has splits of negligible weight

@@ -217,3 +217,25 @@ def test_varlen_decode_serving_batch(gpu_lib):
         K, V = (oracle.decode_bf16(x[b, h // 8, :n]) for x in (kb, vb))
         O, L = oracle.decode_attention(Q, K, V, d ** -0.5)
         check_bf16_gates(og[b, h], O, lg[b, h:h + 1], L, f"(b={b},h={h},len={n})")
+
+
+@pytest.mark.parametrize("ramp", ["up", "down"])
+def test_gqa_splits_of_very_different_weight(gpu_lib, ramp):
+    """Grouped heads over a cache whose key norms double (or halve) every
+    1024 keys, 64 splits: most splits' merge weights underflow."""
+    fa = gpu_lib
+    B, Hq, Hkv, Lkv, d, S = 2, 8, 2, 8192, 128, 64
+    say(f"gqa decode ramped key norms ({ramp}) Hq={Hq} Hkv={Hkv} Lkv={Lkv} splits={S}")
+    qb = fi.bf16_tensor(6900, fi.Q_ID, B, Hq, 1, d)
+    k = np.stack([np.stack([fi.normals(6900 + (ramp == "down"), fi.K_ID, b, h, Lkv, d) for h in range(Hkv)])
+                  for b in range(B)])
+    f = (2.0 ** (np.arange(Lkv) / 1024.0)).astype(np.float32)
+    if ramp == "down":
+        f = f[::-1].copy()
+    kb = fi.f32_to_bf16_bits(k * f[None, None, :, None])
+    vb = fi.bf16_tensor(6900, fi.V_ID, B, Hkv, Lkv, d)
+    scale = d ** -0.5
+    o, lse, _, _ = run(fa, *map(bf16_to_dev, (qb, kb, vb)), B, Hq, Hkv, Lkv, d, S, scale)
+    O, L = oracle.decode_attention_gqa(*map(oracle.decode_bf16, (qb, kb, vb)), scale)
+    check_bf16_gates(dev_to_f64(o)[:, :, 0], O[:, :, 0], dev_to_f64(lse), L[:, :, 0], f"gqa ramp {ramp}",
+                     beyond_floor=True)
