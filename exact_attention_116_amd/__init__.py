@@ -83,11 +83,13 @@ def load(path: str | None = None):
     return lib
 
 
-def _ptr(x):
+def _ptr(x, nbytes: int = 0, name: str = "tensor"):
     """Device address of a tensor (``data_ptr()``), an int (taken as a device
-    address as is), or None.  A tensor must live on a GPU and be contiguous:
-    the kernels read the dense layouts ``include/fa.h`` states, and a host
-    address handed to a kernel would fault the device."""
+    address as is), or None.  A tensor must live on a GPU, be contiguous and
+    hold at least ``nbytes`` bytes: the kernels read and write the dense
+    layouts ``include/fa.h`` states, and a host address or a short buffer
+    handed to a kernel would fault the device.  The C entry points see plain
+    pointers and cannot check sizes; this is where they are checked."""
     if x is None:
         return None
     if isinstance(x, int):
@@ -96,7 +98,25 @@ def _ptr(x):
         raise FaError(FA_ERR_INVALID_ARG, "tensor arguments must be GPU tensors")
     if not x.is_contiguous():
         raise FaError(FA_ERR_INVALID_ARG, "tensor arguments must be contiguous")
+    have = x.numel() * x.element_size()
+    if nbytes > 0 and have < nbytes:
+        raise FaError(FA_ERR_INVALID_ARG, f"{name} holds {have} bytes; the call needs {nbytes}")
     return x.data_ptr()
+
+
+def _n(*dims) -> int:
+    """Product of the dimensions (0 if any is negative: the library rejects those)."""
+    r = 1
+    for v in dims:
+        v = int(v)
+        if v < 0:
+            return 0
+        r *= v
+    return r
+
+
+_IN_BYTES = {FA_BF16: 2, FA_FP16: 2, FA_FP8_E4M3: 1}
+_OUT_BYTES = {FA_BF16: 2, FA_FP16: 2, FA_FP32: 4}
 
 
 def _stream(s):
@@ -124,20 +144,27 @@ def fa_last_error() -> str:
 
 def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal):
     """bf16 [B,H,N,d] q, k, v -> bf16 o, fp32 lse [B,H,N]; default stream."""
-    _check(load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
-                         float(scale), int(bool(causal))), "fa_fwd")
+    t, r = 2 * _n(B, H, N, d), 4 * _n(B, H, N)
+    _check(load().fa_fwd(_ptr(q, t, "q"), _ptr(k, t, "k"), _ptr(v, t, "v"), _ptr(o, t, "o"),
+                         _ptr(lse, r, "lse"), B, H, N, d, float(scale), int(bool(causal))), "fa_fwd")
 
 
 def fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, in_dtype=FA_BF16, out_dtype=FA_BF16,
               q_scale=None, k_scale=None, v_scale=None, stream=None):
-    p = fa_fwd_params(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(q_scale),
-                      _ptr(k_scale), _ptr(v_scale), in_dtype, out_dtype, B, H, N, d,
-                      float(scale), int(bool(causal)), _stream(stream))
+    t = _IN_BYTES.get(in_dtype, 0) * _n(B, H, N, d)
+    to = _OUT_BYTES.get(out_dtype, 0) * _n(B, H, N, d)
+    sc = 4 * _n(B, H, (int(N) + 63) // 64)
+    p = fa_fwd_params(_ptr(q, t, "q"), _ptr(k, t, "k"), _ptr(v, t, "v"), _ptr(o, to, "o"),
+                      _ptr(lse, 4 * _n(B, H, N), "lse"), _ptr(q_scale, sc, "q_scale"),
+                      _ptr(k_scale, sc, "k_scale"), _ptr(v_scale, sc, "v_scale"), in_dtype,
+                      out_dtype, B, H, N, d, float(scale), int(bool(causal)), _stream(stream))
     _check(load().fa_fwd_ex(ctypes.byref(p)), "fa_fwd_ex")
 
 
 def fa_decode_splitkv(q, kcache, vcache, o, B, H, Lkv, d, num_splits):
-    _check(load().fa_decode_splitkv(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(o), B, H, Lkv, d,
+    t, c = 2 * _n(B, H, d), 2 * _n(B, H, Lkv, d)
+    _check(load().fa_decode_splitkv(_ptr(q, t, "q"), _ptr(kcache, c, "kcache"),
+                                    _ptr(vcache, c, "vcache"), _ptr(o, t, "o"), B, H, Lkv, d,
                                     num_splits), "fa_decode_splitkv")
 
 
@@ -147,8 +174,11 @@ def fa_decode_workspace_bytes(B, H, d, num_splits) -> int:
 
 def fa_decode_splitkv_ex(q, kcache, vcache, o, lse, B, H, Lkv, d, num_splits, scale, workspace,
                          workspace_bytes, stream=None):
-    _check(load().fa_decode_splitkv_ex(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(o), _ptr(lse),
-                                       B, H, Lkv, d, num_splits, float(scale), _ptr(workspace),
+    t, c = 2 * _n(B, H, d), 2 * _n(B, H, Lkv, d)
+    _check(load().fa_decode_splitkv_ex(_ptr(q, t, "q"), _ptr(kcache, c, "kcache"),
+                                       _ptr(vcache, c, "vcache"), _ptr(o, t, "o"),
+                                       _ptr(lse, 4 * _n(B, H), "lse"), B, H, Lkv, d, num_splits,
+                                       float(scale), _ptr(workspace, int(workspace_bytes), "workspace"),
                                        int(workspace_bytes), _stream(stream)),
            "fa_decode_splitkv_ex")
 
@@ -156,9 +186,13 @@ def fa_decode_splitkv_ex(q, kcache, vcache, o, lse, B, H, Lkv, d, num_splits, sc
 def fa_decode_splitkv_gqa(q, kcache, vcache, o, lse, B, Hq, Hkv, Lkv, d, num_splits, scale,
                           workspace=None, workspace_bytes=0, stream=None):
     """Grouped K/V heads: q, o bf16 [B,Hq,1,d]; caches bf16 [B,Hkv,Lkv,d]."""
-    _check(load().fa_decode_splitkv_gqa(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(o), _ptr(lse),
-                                        B, Hq, Hkv, Lkv, d, num_splits, float(scale),
-                                        _ptr(workspace), int(workspace_bytes), _stream(stream)),
+    t, c = 2 * _n(B, Hq, d), 2 * _n(B, Hkv, Lkv, d)
+    _check(load().fa_decode_splitkv_gqa(_ptr(q, t, "q"), _ptr(kcache, c, "kcache"),
+                                        _ptr(vcache, c, "vcache"), _ptr(o, t, "o"),
+                                        _ptr(lse, 4 * _n(B, Hq), "lse"), B, Hq, Hkv, Lkv, d,
+                                        num_splits, float(scale),
+                                        _ptr(workspace, int(workspace_bytes), "workspace"),
+                                        int(workspace_bytes), _stream(stream)),
            "fa_decode_splitkv_gqa")
 
 
@@ -169,40 +203,56 @@ def fa_bwd_workspace_bytes(B, H, N) -> int:
 def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, workspace=None,
            workspace_bytes=0, stream=None):
     """bf16 [B,H,N,d] q, k, v, o, dout and fp32 lse [B,H,N] -> bf16 dq, dk, dv."""
-    _check(load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
-                         _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
-                         _ptr(workspace), int(workspace_bytes), _stream(stream)), "fa_bwd")
+    t, r = 2 * _n(B, H, N, d), 4 * _n(B, H, N)
+    _check(load().fa_bwd(_ptr(q, t, "q"), _ptr(k, t, "k"), _ptr(v, t, "v"), _ptr(o, t, "o"),
+                         _ptr(dout, t, "dout"), _ptr(lse, r, "lse"), _ptr(dq, t, "dq"),
+                         _ptr(dk, t, "dk"), _ptr(dv, t, "dv"), B, H, N, d, float(scale),
+                         int(bool(causal)), _ptr(workspace, int(workspace_bytes), "workspace"),
+                         int(workspace_bytes), _stream(stream)), "fa_bwd")
 
 
 def fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype=FA_BF16,
               workspace=None, workspace_bytes=0, stream=None):
     """fa_bwd with the tensor type as an argument: FA_BF16 or FA_FP16."""
-    _check(load().fa_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
-                            _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
-                            int(dtype), _ptr(workspace), int(workspace_bytes), _stream(stream)),
+    t, r = 2 * _n(B, H, N, d), 4 * _n(B, H, N)
+    _check(load().fa_bwd_ex(_ptr(q, t, "q"), _ptr(k, t, "k"), _ptr(v, t, "v"), _ptr(o, t, "o"),
+                            _ptr(dout, t, "dout"), _ptr(lse, r, "lse"), _ptr(dq, t, "dq"),
+                            _ptr(dk, t, "dk"), _ptr(dv, t, "dv"), B, H, N, d, float(scale),
+                            int(bool(causal)), int(dtype),
+                            _ptr(workspace, int(workspace_bytes), "workspace"),
+                            int(workspace_bytes), _stream(stream)),
            "fa_bwd_ex")
 
 
 def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, max_seqlen_q, max_seqlen_k,
                   total_q, total_k, d, scale, causal, stream=None):
     """Packed bf16 q [total_q,H,d], k, v [total_k,H,d] -> o, fp32 lse [H,total_q]."""
-    _check(load().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, H, max_seqlen_q,
+    tq, tk, cu = 2 * _n(total_q, H, d), 2 * _n(total_k, H, d), 4 * _n(int(B) + 1)
+    _check(load().fa_fwd_varlen(_ptr(q, tq, "q"), _ptr(k, tk, "k"), _ptr(v, tk, "v"),
+                                _ptr(o, tq, "o"), _ptr(lse, 4 * _n(H, total_q), "lse"),
+                                _ptr(cu_seqlens_q, cu, "cu_seqlens_q"),
+                                _ptr(cu_seqlens_k, cu, "cu_seqlens_k"), B, H, max_seqlen_q,
                                 max_seqlen_k, total_q, total_k, d, float(scale),
                                 int(bool(causal)), _stream(stream)), "fa_fwd_varlen")
 
 
 def fa_fp8_quantize(x, signs, codes, scales, B, H, N, d, stream=None):
     """bf16 [B,H,N,d] -> E4M3FN codes + fp32 [B,H,ceil(N/64)] scales; signs [d] rotates."""
-    _check(load().fa_fp8_quantize(_ptr(x), _ptr(signs), _ptr(codes), _ptr(scales), B, H, N, d,
-                                  _stream(stream)), "fa_fp8_quantize")
+    _check(load().fa_fp8_quantize(_ptr(x, 2 * _n(B, H, N, d), "x"), _ptr(signs, 4 * _n(d), "signs"),
+                                  _ptr(codes, _n(B, H, N, d), "codes"),
+                                  _ptr(scales, 4 * _n(B, H, (int(N) + 63) // 64), "scales"),
+                                  B, H, N, d, _stream(stream)), "fa_fp8_quantize")
 
 
 def fa_decode_splitkv_varlen(q, kcache, vcache, o, lse, seqlens_k, B, Hq, Hkv, Lkv, d, num_splits,
                              scale, workspace=None, workspace_bytes=0, stream=None):
     """Grouped decode over padded caches [B,Hkv,Lkv,d] with int32 seqlens_k [B] (device)."""
-    _check(load().fa_decode_splitkv_varlen(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(o),
-                                           _ptr(lse), _ptr(seqlens_k), B, Hq, Hkv, Lkv, d,
-                                           num_splits, float(scale), _ptr(workspace),
+    t, c = 2 * _n(B, Hq, d), 2 * _n(B, Hkv, Lkv, d)
+    _check(load().fa_decode_splitkv_varlen(_ptr(q, t, "q"), _ptr(kcache, c, "kcache"),
+                                           _ptr(vcache, c, "vcache"), _ptr(o, t, "o"),
+                                           _ptr(lse, 4 * _n(B, Hq), "lse"),
+                                           _ptr(seqlens_k, 4 * _n(B), "seqlens_k"), B, Hq, Hkv,
+                                           Lkv, d, num_splits, float(scale),
+                                           _ptr(workspace, int(workspace_bytes), "workspace"),
                                            int(workspace_bytes), _stream(stream)),
            "fa_decode_splitkv_varlen")
