@@ -9,20 +9,27 @@
 //
 // gfx950 mapping (shared with the bf16 kernel: one wave per 32 queries, the
 // transposed score tile S^T = K Q^T so that each lane owns one query)
-//  * Both products run on the 32x32x64 fp8 MFMA (unscaled form): S^T from
-//    K codes (LDS, A operand) and Q codes (VGPRs, B operand); O^T += V^T P^T
-//    from V codes (LDS, read transposed) and P rounded to E4M3FN (B operand).
+//  * Both products run on the 32x32x64 fp8 MFMA: S^T from K codes (LDS, A
+//    operand) and Q codes (VGPRs, B operand); O^T += V^T P^T from V codes
+//    (LDS, read transposed, with a power-of-two block scale) and P rounded
+//    to E4M3FN (B operand).
 //  * A key tile is 128 keys, two scale blocks of K and of V, and the 32
 //    queries of a wave lie in one scale block of Q.  So the score scale is
 //    scale * log2(e) * s_q * s_k, one scalar per lane and half tile, folded
 //    into the FMA that feeds exp2.
-//  * V's block scale is folded into P before it is rounded: the weights of
-//    scale block t are multiplied by sigma_t = 256 * s_v(t) / max_t s_v(t)
-//    (added to the exp2 argument as log2 sigma_t), and the row sum
-//    accumulates the weights divided by sigma_t.  The accumulator then holds
-//    (256 / max s_v) * sum_j p_j v_j, undone once in the epilogue.
+//  * P is pre-scaled by the constant 256 = 2^8 before it is rounded to
+//    E4M3FN, so the largest weight of a row (exactly 1 whenever the running
+//    max has just moved) stays exact.  A pre-scale that varied per V block
+//    would round that weight by up to 2^-4 in every row dominated by one key.
+//  * V's block scale enters outside the rounding of P.  Write s_v(t) = 2^e_t
+//    * r_t with r_t in [0.5, 1).  The power of two 2^(e_t - e_max) is the
+//    E8M0 scale of the V operand of the scaled fp8 MFMA (each 32x32x64
+//    product covers exactly one 64-key V block), and the accumulator is kept
+//    in units of the current block's r_t: before the products of block t it
+//    is multiplied by r_{t-1} / r_t (merged with the running-max rescale).
+//    The epilogue multiplies by r_last * 2^e_max once.
 //  * The running max is moved only when it would grow by more than 0.75 (base
-//    2), so every weight times sigma_t stays below 256 * 2^0.75 < 448, the
+//    2), so every weight times 256 stays below 256 * 2^0.75 < 448, the
 //    largest E4M3FN value; skipped rescales leave the result exact.
 //  * K and V tiles go from HBM straight to LDS with direct buffer loads (rows
 //    past N read as 0 through the buffer range), double-buffered, the loads
@@ -34,12 +41,21 @@ namespace fa {
 
 namespace {
 constexpr int D = 128;
-constexpr float kPScale = 256.f;
-constexpr float kLazy = 0.75f;  // 256 * 2^0.75 = 430.5 < 448
+constexpr float kLog2PScale = 8.f;  // P is rounded as 256 * p
+constexpr float kLazy = 0.75f;      // 256 * 2^0.75 = 430.5 < 448
+constexpr int kE8M0One = 127;       // E8M0 code of 2^0
 }  // namespace
 
 __device__ __forceinline__ f32x16 mfma32x32x64_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// The same product with the A operand multiplied by 2^(sa - 127): sa is an
+// E8M0 code (the same in every lane here, so it scales all of A); B is
+// unscaled (code 127).
+__device__ __forceinline__ f32x16 mfma32x32x64_fp8_sa(const i32x8& a, const i32x8& b, const f32x16& c,
+                                                      int sa) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, kE8M0One);
 }
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -104,9 +120,12 @@ void fa_fwd_fp8_dl_kernel(const uint8_t* __restrict__ q, const uint8_t* __restri
   const float* ksh = ks + (size_t)bh * nsb;
   const float* vsh = vs + (size_t)bh * nsb;
 
+  // the binary exponent of the head's largest V scale: every block's
+  // power of two is taken relative to it (E8M0 codes <= 127)
   float svmax = 0.f;
   for (int i = lane; i < nsb; i += 64) svmax = fmaxf(svmax, vsh[i]);
   svmax = wave_max(svmax);
+  const int e_max = __builtin_amdgcn_frexp_expf(svmax);
 
   const int q0 = qt * BRW;
   const int qw = q0 + wave * 32;
@@ -182,7 +201,8 @@ void fa_fwd_fp8_dl_kernel(const uint8_t* __restrict__ q, const uint8_t* __restri
 #pragma unroll
   for (int cb = 0; cb < D / 32; ++cb) acc[cb] = f32x16{};
   float m = kNegInf;
-  float l = 0.f;
+  float l = 0.f;                                    // row sum of 256 * p
+  float r_cur = __builtin_amdgcn_frexp_mantf(vsh[0]);  // units of acc
 
   load_tile(0);
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -258,24 +278,43 @@ void fa_fwd_fp8_dl_kernel(const uint8_t* __restrict__ q, const uint8_t* __restri
       float mx = fmaxf(mx0 * ce0, mx1 * ce1);
       mx = max_pair32(mx);
       const float m_cand = fmaxf(m, mx);
+      float alpha = 1.f;
       if (__builtin_amdgcn_ballot_w64(m_cand > m + kLazy)) {
-        const float alpha = (m_cand == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m - m_cand);
+        alpha = (m_cand == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m - m_cand);
         m = m_cand;
         l *= alpha;
-#pragma unroll
-        for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[cb][i] *= alpha;
       }
       const float mref = (m == kNegInf) ? 0.f : m;
+      const float bias = kLog2PScale - mref;
+
+      // V block t = sb0 + hh: E8M0 code of 2^(e_t - e_max) for the product,
+      // and the factor that moves acc from the previous block's units r to
+      // this block's (the half past N, whose keys are all masked, keeps both)
+      int sa[2];
+      float fac[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        if (hh == 0 || h1) {
+          const float sv = vsh[sb0 + hh];
+          const float rt = __builtin_amdgcn_frexp_mantf(sv);
+          sa[hh] = max(kE8M0One + __builtin_amdgcn_frexp_expf(sv) - e_max, 0);
+          fac[hh] = r_cur * __builtin_amdgcn_rcpf(rt);
+          r_cur = rt;
+        } else {
+          sa[hh] = kE8M0One;
+          fac[hh] = 1.f;
+        }
+      }
+      fac[0] *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[cb][i] *= fac[0];
 
       i32x8 pb[2];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const float svt = (hh == 0 || h1) ? vsh[sb0 + hh] : svmax;
         const float ce = hh == 0 ? ce0 : ce1;
-        const float lsig = __builtin_amdgcn_logf(kPScale * (svt / svmax));
-        const float bias = lsig - mref;
         float p[2][16];
         float tsum = 0.f;
 #pragma unroll
@@ -285,7 +324,7 @@ void fa_fwd_fp8_dl_kernel(const uint8_t* __restrict__ q, const uint8_t* __restri
             p[bb][i] = __builtin_amdgcn_exp2f(fmaf(s[2 * hh + bb][i], ce, bias));
             tsum += p[bb][i];
           }
-        l = fmaf(tsum, __builtin_amdgcn_exp2f(-lsig), l);
+        l += tsum;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const int bb = t >> 2, i0 = 4 * (t & 3);
@@ -314,7 +353,8 @@ void fa_fwd_fp8_dl_kernel(const uint8_t* __restrict__ q, const uint8_t* __restri
           }
           if (i >= PD) {
             const int x = i - PD, hh = x / (D / 32), cb = x % (D / 32);
-            acc[cb] = mfma32x32x64_fp8(vf[x], pb[hh], acc[cb]);
+            // the second block's products start from acc in its units
+            acc[cb] = mfma32x32x64_fp8_sa(vf[x], pb[hh], hh == 0 ? acc[cb] : acc[cb] * fac[1], sa[hh]);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -326,7 +366,8 @@ void fa_fwd_fp8_dl_kernel(const uint8_t* __restrict__ q, const uint8_t* __restri
   }
 
   l = sum_pair32(l);
-  const float fac = (svmax / kPScale) / l;
+  // acc holds 256 * sum_t (r_t / r_last) sum_j p_j code_j 2^(e_t - e_max)
+  const float fac = __builtin_amdgcn_ldexpf(r_cur, e_max) / l;
   if (my_q < N) {
     const size_t row = (size_t)bh * N + my_q;
 #pragma unroll
@@ -338,7 +379,7 @@ void fa_fwd_fp8_dl_kernel(const uint8_t* __restrict__ q, const uint8_t* __restri
         const float o2 = acc[cb][4 * ii + 2] * fac, o3 = acc[cb][4 * ii + 3] * fac;
         *reinterpret_cast<u32x2*>(o + row * D + d0) = u32x2{pack_bf16(o0, o1), pack_bf16(o2, o3)};
       }
-    if (g == 0) lse[row] = (m + __builtin_amdgcn_logf(l)) * kLn2;
+    if (g == 0) lse[row] = (m + __builtin_amdgcn_logf(l) - kLog2PScale) * kLn2;
   }
 }
 

@@ -2,18 +2,18 @@
 
 The oracle runs on the dequantised inputs (code value times block scale, in
 float64).  Gates, stated for a kernel that rounds the probabilities to
-E4M3FN before the P*V product:
+E4M3FN before the P*V product, and fixed independently of the kernel:
   F1  LSE relative error <= 1e-3 (denominator max(|LSE|, 1));
   F2  every output element within the oracle's elementwise bound
-      ``oracle.fp8_p_error_bound``, evaluated with the smallest pre-scale the
-      kernel applies to P in that head (256 * min s_v / max s_v);
-  F3  mean-abs error <= 1.25 x (the mean-abs error of
-      ``oracle.fp8_p_attention``, exact attention with only P rounded to
-      E4M3FN with the kernel's documented pre-scale) + 1e-4, over the sampled
-      rows of the full-size workload (B=4, H=16, N=8192): the kernel adds
-      little beyond the rounding of P that the fp8 product implies.  On the
-      small edge shapes, where a mean over few elements is noisy, it is
-      reported, not gated.
+      ``oracle.fp8_p_error_bound`` for probabilities rounded as 256 * p
+      (pre-scale sigma = 256 = 2^8 for every key);
+  F3  mean-abs error <= 3e-3 over the checked outputs of the full-size
+      workload (B=4, H=16, N=8192, causal, x20 outliers): every (batch,
+      head), on the first and last row of every 128-query tile plus 512
+      random rows per head.  For scale, the mean error of
+      ``oracle.fp8_p_attention`` (exact attention with only P rounded as
+      256 * p) is printed beside it; on the small edge shapes, where a mean
+      over few elements is noisy, the mean is reported, not gated.
 The max-abs error is printed beside them.
 """
 import numpy as np
@@ -26,8 +26,8 @@ from _gpu_util import dev_to_f64, lse_rel, say, u8_to_dev
 
 pytestmark = pytest.mark.gpu
 
-F3_FACTOR = 1.25
-F3_SLACK = 1e-4
+F3_MEAN_ABS = 3e-3
+P_PRESCALE = 256.0
 LSE_REL = 1e-3
 
 
@@ -42,29 +42,22 @@ def run_fp8(fa, codes, scales, B, H, N, d, scale, causal):
     return dev_to_f64(o), dev_to_f64(lse)
 
 
-def p_prescale_min(v_scales_head):
-    s = np.asarray(v_scales_head, np.float64)
-    return 256.0 * s.min() / s.max()
-
-
-def p_prescale_per_key(v_scales_head, Nk):
-    """The pre-scale the kernel documents for key j: 256 * s_v(j // 64) / max s_v."""
-    s = np.asarray(v_scales_head, np.float64)
-    return (256.0 * s / s.max())[np.arange(Nk) // 64]
-
-
-def check_head(og, lg, q, k, v, vsc, scale, causal, rows, what):
-    O, L, Bnd = oracle.fp8_p_error_bound(q[rows], k, v, scale, causal, p_prescale_min(vsc),
-                                         qidx=rows)
-    Om = oracle.fp8_p_attention(q[rows], k, v, scale, causal, p_prescale_per_key(vsc, k.shape[0]),
-                                qidx=rows)
+def check_head(og, lg, q, k, v, scale, causal, rows, what, model=False):
+    """F1 and F2 for the rows ``rows`` of one (b, h); returns the abs errors
+    and, with ``model``, those of the P-rounding yardstick."""
+    O, L, Bnd = oracle.fp8_p_error_bound(q[rows], k, v, scale, causal, P_PRESCALE, qidx=rows)
     err = np.abs(og - O)
-    err_model = np.abs(Om - O)
     lr = lse_rel(lg, L)
     ratio = float((err / Bnd).max())
-    say(f"  {what}: max_abs={err.max():.3e} mean_abs={err.mean():.3e} "
-        f"(P-rounding model {err_model.mean():.3e}) lse_rel={lr.max():.3e} "
-        f"max err/bound={ratio:.3f}")
+    err_model = None
+    extra = ""
+    if model:
+        Om = oracle.fp8_p_attention(q[rows], k, v, scale, causal, np.full(k.shape[0], P_PRESCALE),
+                                    qidx=rows)
+        err_model = np.abs(Om - O)
+        extra = f" (P-rounding model {err_model.mean():.3e})"
+    say(f"  {what}: max_abs={err.max():.3e} mean_abs={err.mean():.3e}{extra} "
+        f"lse_rel={lr.max():.3e} max err/bound={ratio:.3f}")
     assert np.all(np.isfinite(og)), f"{what}: non-finite output"
     assert lr.max() <= LSE_REL, f"{what}: LSE relative {lr.max()}"
     assert np.all(err <= Bnd), f"{what}: error above the fp8 bound (ratio {ratio})"
@@ -109,21 +102,31 @@ def test_fp8_edge_shapes(gpu_lib, N, causal):
     codes, scales = gen(wid, B, H, N, d, outlier_p=1e-2)
     og, lg = run_fp8(fa, codes, scales, B, H, N, d, d ** -0.5, causal)
     deq = [oracle.dequant_fp8_rows(c, s) for c, s in zip(codes, scales)]
-    errs = []
+    errs, errs_model = [], []
     for b in range(B):
         for h in range(H):
-            errs.append(check_head(og[b, h], lg[b, h], deq[0][b, h], deq[1][b, h], deq[2][b, h],
-                                   scales[2][b, h], d ** -0.5, causal, np.arange(N),
-                                   f"(b={b},h={h})"))
+            e, em = check_head(og[b, h], lg[b, h], deq[0][b, h], deq[1][b, h], deq[2][b, h],
+                               d ** -0.5, causal, np.arange(N), f"(b={b},h={h})", model=True)
+            errs.append(e)
+            errs_model.append(em)
     # F3 is a gate on the long rows of the measured workload; rows of a few
     # keys carry the full 2^-4 rounding of P, so here it is only reported.
-    mean = float(np.mean(np.concatenate([e.ravel() for e, _ in errs])))
-    mean_model = float(np.mean(np.concatenate([e.ravel() for _, e in errs])))
+    mean = float(np.mean(np.concatenate([e.ravel() for e in errs])))
+    mean_model = float(np.mean(np.concatenate([e.ravel() for e in errs_model])))
     say(f"  mean-abs {mean:.3e} (P-rounding model {mean_model:.3e})")
 
 
+def full_size_rows(N, tile, seed, n_random=512):
+    """The first and last row of every ``tile``-query tile plus ``n_random``
+    distinct random rows."""
+    edges = np.r_[np.arange(0, N, tile), np.minimum(np.arange(tile - 1, N + tile - 1, tile), N - 1)]
+    rnd = np.random.default_rng(seed).choice(N, min(n_random, N), replace=False)
+    return np.unique(np.r_[edges, rnd])
+
+
 def test_fp8_full_size(gpu_lib):
-    """B=4, H=16, N=8192, d=128, causal, 0.1% x20 outliers: sampled heads and rows."""
+    """B=4, H=16, N=8192, d=128, causal, 0.1% x20 outliers: every (b, h) on
+    the tile-edge rows and 512 random rows each."""
     fa = gpu_lib
     w = fi.WORKLOADS[5]
     say(f"fp8 {w.name}: generating")
@@ -131,17 +134,21 @@ def test_fp8_full_size(gpu_lib):
     say("fp8 full size: running")
     og, lg = run_fp8(fa, codes, scales, w.B, w.H, w.N, w.d, w.scale, True)
     assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg))
-    rows = np.unique(np.r_[0:128, 4032:4160, 8064:8192,
-                           np.random.default_rng(55).choice(w.N, 256, replace=False)])
-    errs = []
-    for b, h in [(0, 0), (1, 9), (3, 15)]:
-        q, k, v = (oracle.dequant_fp8_rows(c[b, h], s[b, h]) for c, s in zip(codes, scales))
-        errs.append(check_head(og[b, h, rows], lg[b, h, rows], q, k, v, scales[2][b, h], w.scale,
-                               True, rows, f"(b={b},h={h}) rows={len(rows)}"))
-    mean = float(np.mean(np.concatenate([e.ravel() for e, _ in errs])))
-    mean_model = float(np.mean(np.concatenate([e.ravel() for _, e in errs])))
-    say(f"  mean-abs over the sampled rows: {mean:.3e}; P-rounding model {mean_model:.3e}")
-    assert mean <= F3_FACTOR * mean_model + F3_SLACK, (mean, mean_model)
+    errs, errs_model = [], []
+    for b in range(w.B):
+        for h in range(w.H):
+            rows = full_size_rows(w.N, 128, 5500 + w.H * b + h)
+            q, k, v = (oracle.dequant_fp8_rows(c[b, h], s[b, h]) for c, s in zip(codes, scales))
+            e, em = check_head(og[b, h, rows], lg[b, h, rows], q, k, v, w.scale, True, rows,
+                               f"(b={b},h={h}) rows={len(rows)}", model=(h % 8 == 0))
+            errs.append(e)
+            if em is not None:
+                errs_model.append(em)
+    mean = float(np.mean(np.concatenate([e.ravel() for e in errs])))
+    mean_model = float(np.mean(np.concatenate([e.ravel() for e in errs_model])))
+    say(f"  mean-abs over all heads' checked rows: {mean:.3e} (F3 gate {F3_MEAN_ABS}); "
+        f"P-rounding model on heads h=0,8: {mean_model:.3e}")
+    assert mean <= F3_MEAN_ABS, (mean, mean_model)
 
 
 def test_fp8_deterministic_and_in_bounds(gpu_lib):

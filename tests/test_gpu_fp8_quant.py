@@ -16,7 +16,7 @@ import torch
 import fa_inputs as fi
 import oracle
 from _gpu_util import bf16_to_dev, dev_to_f64, say
-from test_gpu_fp8 import check_head, p_prescale_per_key
+from test_gpu_fp8 import check_head
 
 pytestmark = pytest.mark.gpu
 
@@ -109,8 +109,7 @@ def test_rotated_fp8_forward(gpu_lib):
             dq, dk, dv = (oracle.dequant_fp8_rows(c[0, h].cpu().numpy(), s[0, h].cpu().numpy())
                           for c, s in ((qc, qs), (kc, ks), (vc, vs)))
             rows = np.arange(N)
-            check_head(og[0, h], lg[0, h], dq, dk, dv, vs[0, h].cpu().numpy(), scale, True, rows,
-                       f"rot={rot} h={h}")
+            check_head(og[0, h], lg[0, h], dq, dk, dv, scale, True, rows, f"rot={rot} h={h}")
             Oex, _ = oracle.attention(*(oracle.decode_bf16(x[0, h]) for x in xs), scale, True)
             e_exact.append(np.abs(og[0, h] - Oex))
         errs[rot] = float(np.sqrt(np.mean(np.concatenate(e_exact) ** 2)))
