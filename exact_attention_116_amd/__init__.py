@@ -83,13 +83,22 @@ def load(path: str | None = None):
     return lib
 
 
-def _ptr(x, nbytes: int = 0, name: str = "tensor"):
+# torch dtype names accepted for each kind of tensor argument
+BF16, F16, F32, I32 = ("torch.bfloat16",), ("torch.float16",), ("torch.float32",), ("torch.int32",)
+U8 = ("torch.uint8", "torch.int8", "torch.float8_e4m3fn")   # E4M3FN codes as bytes
+_IN_DT = {0: BF16, 3: F16, 2: U8}          # FA_BF16, FA_FP16, FA_FP8_E4M3
+_OUT_DT = {0: BF16, 3: F16, 1: F32}        # FA_BF16, FA_FP16, FA_FP32
+
+
+def _ptr(x, nbytes: int = 0, name: str = "tensor", dtypes=None):
     """Device address of a tensor (``data_ptr()``), an int (taken as a device
-    address as is), or None.  A tensor must live on a GPU, be contiguous and
-    hold at least ``nbytes`` bytes: the kernels read and write the dense
-    layouts ``include/fa.h`` states, and a host address or a short buffer
-    handed to a kernel would fault the device.  The C entry points see plain
-    pointers and cannot check sizes; this is where they are checked."""
+    address as is), or None.  A tensor must live on a GPU, be contiguous,
+    hold at least ``nbytes`` bytes and, when ``dtypes`` is given, have one of
+    those dtypes: the kernels read and write the dense layouts and element
+    types ``include/fa.h`` states, and a host address, a short buffer or
+    another element type handed to a kernel would fault the device or be
+    read as the wrong numbers.  The C entry points see plain pointers and
+    cannot check any of this; this is where it is checked."""
     if x is None:
         return None
     if isinstance(x, int):
@@ -101,6 +110,9 @@ def _ptr(x, nbytes: int = 0, name: str = "tensor"):
     have = x.numel() * x.element_size()
     if nbytes > 0 and have < nbytes:
         raise FaError(FA_ERR_INVALID_ARG, f"{name} holds {have} bytes; the call needs {nbytes}")
+    if dtypes is not None and str(x.dtype) not in dtypes:
+        raise FaError(FA_ERR_INVALID_ARG, f"{name} has dtype {x.dtype}; the call needs "
+                                          f"{' or '.join(dtypes)}")
     return x.data_ptr()
 
 
@@ -145,8 +157,9 @@ def fa_last_error() -> str:
 def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal):
     """bf16 [B,H,N,d] q, k, v -> bf16 o, fp32 lse [B,H,N]; default stream."""
     t, r = 2 * _n(B, H, N, d), 4 * _n(B, H, N)
-    _check(load().fa_fwd(_ptr(q, t, "q"), _ptr(k, t, "k"), _ptr(v, t, "v"), _ptr(o, t, "o"),
-                         _ptr(lse, r, "lse"), B, H, N, d, float(scale), int(bool(causal))), "fa_fwd")
+    _check(load().fa_fwd(_ptr(q, t, "q", BF16), _ptr(k, t, "k", BF16), _ptr(v, t, "v", BF16),
+                         _ptr(o, t, "o", BF16), _ptr(lse, r, "lse", F32), B, H, N, d, float(scale),
+                         int(bool(causal))), "fa_fwd")
 
 
 def fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, in_dtype=FA_BF16, out_dtype=FA_BF16,
@@ -154,18 +167,20 @@ def fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, in_dtype=FA_BF16, out_
     t = _IN_BYTES.get(in_dtype, 0) * _n(B, H, N, d)
     to = _OUT_BYTES.get(out_dtype, 0) * _n(B, H, N, d)
     sc = 4 * _n(B, H, (int(N) + 63) // 64)
-    p = fa_fwd_params(_ptr(q, t, "q"), _ptr(k, t, "k"), _ptr(v, t, "v"), _ptr(o, to, "o"),
-                      _ptr(lse, 4 * _n(B, H, N), "lse"), _ptr(q_scale, sc, "q_scale"),
-                      _ptr(k_scale, sc, "k_scale"), _ptr(v_scale, sc, "v_scale"), in_dtype,
-                      out_dtype, B, H, N, d, float(scale), int(bool(causal)), _stream(stream))
+    di, do_ = _IN_DT.get(in_dtype), _OUT_DT.get(out_dtype)
+    p = fa_fwd_params(_ptr(q, t, "q", di), _ptr(k, t, "k", di), _ptr(v, t, "v", di),
+                      _ptr(o, to, "o", do_), _ptr(lse, 4 * _n(B, H, N), "lse", F32),
+                      _ptr(q_scale, sc, "q_scale", F32), _ptr(k_scale, sc, "k_scale", F32),
+                      _ptr(v_scale, sc, "v_scale", F32), in_dtype, out_dtype, B, H, N, d,
+                      float(scale), int(bool(causal)), _stream(stream))
     _check(load().fa_fwd_ex(ctypes.byref(p)), "fa_fwd_ex")
 
 
 def fa_decode_splitkv(q, kcache, vcache, o, B, H, Lkv, d, num_splits):
     t, c = 2 * _n(B, H, d), 2 * _n(B, H, Lkv, d)
-    _check(load().fa_decode_splitkv(_ptr(q, t, "q"), _ptr(kcache, c, "kcache"),
-                                    _ptr(vcache, c, "vcache"), _ptr(o, t, "o"), B, H, Lkv, d,
-                                    num_splits), "fa_decode_splitkv")
+    _check(load().fa_decode_splitkv(_ptr(q, t, "q", BF16), _ptr(kcache, c, "kcache", BF16),
+                                    _ptr(vcache, c, "vcache", BF16), _ptr(o, t, "o", BF16), B, H,
+                                    Lkv, d, num_splits), "fa_decode_splitkv")
 
 
 def fa_decode_workspace_bytes(B, H, d, num_splits) -> int:
@@ -175,9 +190,9 @@ def fa_decode_workspace_bytes(B, H, d, num_splits) -> int:
 def fa_decode_splitkv_ex(q, kcache, vcache, o, lse, B, H, Lkv, d, num_splits, scale, workspace,
                          workspace_bytes, stream=None):
     t, c = 2 * _n(B, H, d), 2 * _n(B, H, Lkv, d)
-    _check(load().fa_decode_splitkv_ex(_ptr(q, t, "q"), _ptr(kcache, c, "kcache"),
-                                       _ptr(vcache, c, "vcache"), _ptr(o, t, "o"),
-                                       _ptr(lse, 4 * _n(B, H), "lse"), B, H, Lkv, d, num_splits,
+    _check(load().fa_decode_splitkv_ex(_ptr(q, t, "q", BF16), _ptr(kcache, c, "kcache", BF16),
+                                       _ptr(vcache, c, "vcache", BF16), _ptr(o, t, "o", BF16),
+                                       _ptr(lse, 4 * _n(B, H), "lse", F32), B, H, Lkv, d, num_splits,
                                        float(scale), _ptr(workspace, int(workspace_bytes), "workspace"),
                                        int(workspace_bytes), _stream(stream)),
            "fa_decode_splitkv_ex")
@@ -187,9 +202,9 @@ def fa_decode_splitkv_gqa(q, kcache, vcache, o, lse, B, Hq, Hkv, Lkv, d, num_spl
                           workspace=None, workspace_bytes=0, stream=None):
     """Grouped K/V heads: q, o bf16 [B,Hq,1,d]; caches bf16 [B,Hkv,Lkv,d]."""
     t, c = 2 * _n(B, Hq, d), 2 * _n(B, Hkv, Lkv, d)
-    _check(load().fa_decode_splitkv_gqa(_ptr(q, t, "q"), _ptr(kcache, c, "kcache"),
-                                        _ptr(vcache, c, "vcache"), _ptr(o, t, "o"),
-                                        _ptr(lse, 4 * _n(B, Hq), "lse"), B, Hq, Hkv, Lkv, d,
+    _check(load().fa_decode_splitkv_gqa(_ptr(q, t, "q", BF16), _ptr(kcache, c, "kcache", BF16),
+                                        _ptr(vcache, c, "vcache", BF16), _ptr(o, t, "o", BF16),
+                                        _ptr(lse, 4 * _n(B, Hq), "lse", F32), B, Hq, Hkv, Lkv, d,
                                         num_splits, float(scale),
                                         _ptr(workspace, int(workspace_bytes), "workspace"),
                                         int(workspace_bytes), _stream(stream)),
@@ -204,9 +219,10 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, workspa
            workspace_bytes=0, stream=None):
     """bf16 [B,H,N,d] q, k, v, o, dout and fp32 lse [B,H,N] -> bf16 dq, dk, dv."""
     t, r = 2 * _n(B, H, N, d), 4 * _n(B, H, N)
-    _check(load().fa_bwd(_ptr(q, t, "q"), _ptr(k, t, "k"), _ptr(v, t, "v"), _ptr(o, t, "o"),
-                         _ptr(dout, t, "dout"), _ptr(lse, r, "lse"), _ptr(dq, t, "dq"),
-                         _ptr(dk, t, "dk"), _ptr(dv, t, "dv"), B, H, N, d, float(scale),
+    _check(load().fa_bwd(_ptr(q, t, "q", BF16), _ptr(k, t, "k", BF16), _ptr(v, t, "v", BF16),
+                         _ptr(o, t, "o", BF16), _ptr(dout, t, "dout", BF16), _ptr(lse, r, "lse", F32),
+                         _ptr(dq, t, "dq", BF16), _ptr(dk, t, "dk", BF16), _ptr(dv, t, "dv", BF16),
+                         B, H, N, d, float(scale),
                          int(bool(causal)), _ptr(workspace, int(workspace_bytes), "workspace"),
                          int(workspace_bytes), _stream(stream)), "fa_bwd")
 
@@ -215,9 +231,11 @@ def fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtyp
               workspace=None, workspace_bytes=0, stream=None):
     """fa_bwd with the tensor type as an argument: FA_BF16 or FA_FP16."""
     t, r = 2 * _n(B, H, N, d), 4 * _n(B, H, N)
-    _check(load().fa_bwd_ex(_ptr(q, t, "q"), _ptr(k, t, "k"), _ptr(v, t, "v"), _ptr(o, t, "o"),
-                            _ptr(dout, t, "dout"), _ptr(lse, r, "lse"), _ptr(dq, t, "dq"),
-                            _ptr(dk, t, "dk"), _ptr(dv, t, "dv"), B, H, N, d, float(scale),
+    dt = {FA_BF16: BF16, FA_FP16: F16}.get(int(dtype))
+    _check(load().fa_bwd_ex(_ptr(q, t, "q", dt), _ptr(k, t, "k", dt), _ptr(v, t, "v", dt),
+                            _ptr(o, t, "o", dt), _ptr(dout, t, "dout", dt), _ptr(lse, r, "lse", F32),
+                            _ptr(dq, t, "dq", dt), _ptr(dk, t, "dk", dt), _ptr(dv, t, "dv", dt),
+                            B, H, N, d, float(scale),
                             int(bool(causal)), int(dtype),
                             _ptr(workspace, int(workspace_bytes), "workspace"),
                             int(workspace_bytes), _stream(stream)),
@@ -228,19 +246,21 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, max_seqlen_
                   total_q, total_k, d, scale, causal, stream=None):
     """Packed bf16 q [total_q,H,d], k, v [total_k,H,d] -> o, fp32 lse [H,total_q]."""
     tq, tk, cu = 2 * _n(total_q, H, d), 2 * _n(total_k, H, d), 4 * _n(int(B) + 1)
-    _check(load().fa_fwd_varlen(_ptr(q, tq, "q"), _ptr(k, tk, "k"), _ptr(v, tk, "v"),
-                                _ptr(o, tq, "o"), _ptr(lse, 4 * _n(H, total_q), "lse"),
-                                _ptr(cu_seqlens_q, cu, "cu_seqlens_q"),
-                                _ptr(cu_seqlens_k, cu, "cu_seqlens_k"), B, H, max_seqlen_q,
+    _check(load().fa_fwd_varlen(_ptr(q, tq, "q", BF16), _ptr(k, tk, "k", BF16),
+                                _ptr(v, tk, "v", BF16), _ptr(o, tq, "o", BF16),
+                                _ptr(lse, 4 * _n(H, total_q), "lse", F32),
+                                _ptr(cu_seqlens_q, cu, "cu_seqlens_q", I32),
+                                _ptr(cu_seqlens_k, cu, "cu_seqlens_k", I32), B, H, max_seqlen_q,
                                 max_seqlen_k, total_q, total_k, d, float(scale),
                                 int(bool(causal)), _stream(stream)), "fa_fwd_varlen")
 
 
 def fa_fp8_quantize(x, signs, codes, scales, B, H, N, d, stream=None):
     """bf16 [B,H,N,d] -> E4M3FN codes + fp32 [B,H,ceil(N/64)] scales; signs [d] rotates."""
-    _check(load().fa_fp8_quantize(_ptr(x, 2 * _n(B, H, N, d), "x"), _ptr(signs, 4 * _n(d), "signs"),
-                                  _ptr(codes, _n(B, H, N, d), "codes"),
-                                  _ptr(scales, 4 * _n(B, H, (int(N) + 63) // 64), "scales"),
+    _check(load().fa_fp8_quantize(_ptr(x, 2 * _n(B, H, N, d), "x", BF16),
+                                  _ptr(signs, 4 * _n(d), "signs", F32),
+                                  _ptr(codes, _n(B, H, N, d), "codes", U8),
+                                  _ptr(scales, 4 * _n(B, H, (int(N) + 63) // 64), "scales", F32),
                                   B, H, N, d, _stream(stream)), "fa_fp8_quantize")
 
 
@@ -248,10 +268,10 @@ def fa_decode_splitkv_varlen(q, kcache, vcache, o, lse, seqlens_k, B, Hq, Hkv, L
                              scale, workspace=None, workspace_bytes=0, stream=None):
     """Grouped decode over padded caches [B,Hkv,Lkv,d] with int32 seqlens_k [B] (device)."""
     t, c = 2 * _n(B, Hq, d), 2 * _n(B, Hkv, Lkv, d)
-    _check(load().fa_decode_splitkv_varlen(_ptr(q, t, "q"), _ptr(kcache, c, "kcache"),
-                                           _ptr(vcache, c, "vcache"), _ptr(o, t, "o"),
-                                           _ptr(lse, 4 * _n(B, Hq), "lse"),
-                                           _ptr(seqlens_k, 4 * _n(B), "seqlens_k"), B, Hq, Hkv,
+    _check(load().fa_decode_splitkv_varlen(_ptr(q, t, "q", BF16), _ptr(kcache, c, "kcache", BF16),
+                                           _ptr(vcache, c, "vcache", BF16), _ptr(o, t, "o", BF16),
+                                           _ptr(lse, 4 * _n(B, Hq), "lse", F32),
+                                           _ptr(seqlens_k, 4 * _n(B), "seqlens_k", I32), B, Hq, Hkv,
                                            Lkv, d, num_splits, float(scale),
                                            _ptr(workspace, int(workspace_bytes), "workspace"),
                                            int(workspace_bytes), _stream(stream)),

@@ -87,12 +87,16 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  *                         value = code * scale (the block quantisation of
  *                         the FlashAttention-3 snippets).  Both products run
  *                         on fp8 matrix cores with fp32 accumulation: the
- *                         unnormalised probabilities of keys in V block t
- *                         (at most 2^0.75 each) are multiplied by
- *                         256 * v_scale[t] / max(v_scale of the head) and
- *                         rounded to E4M3FN for the P*V product; the row sum
- *                         uses the unrounded fp32 values.  d must be 128 and
- *                         out_dtype FA_BF16 (else FA_ERR_UNSUPPORTED).
+ *                         unnormalised probabilities (at most 2^0.75 each)
+ *                         are multiplied by 256 and rounded to E4M3FN for
+ *                         the P*V product, and each V block's scale is
+ *                         applied exactly outside that rounding; the row
+ *                         sum uses the unrounded fp32 values.  Within one
+ *                         (b, h), a V block scale more than 2^127 below
+ *                         the largest has its binary exponent raised to
+ *                         127 below the largest's.
+ *                         d must be 128 and out_dtype FA_BF16 (else
+ *                         FA_ERR_UNSUPPORTED).
  * in_dtype  FA_FP16     : q, k, v IEEE fp16 [B,H,N,d] (the note's "使用注意事项"
  *                         usage notes list FP16 beside BF16); the same
  *                         kernel on the fp16 matrix cores, with P rounded
@@ -178,8 +182,8 @@ fa_status fa_decode_splitkv_ex(const void* q, const void* kcache, const void* vc
  * after the call.  workspace = NULL with workspace_bytes = 0 selects the
  * library-owned workspace (which allocates, see fa_decode_splitkv).
  * One workgroup streams a (batch, K/V head, split) range once for up to 16
- * query heads of its group; groups larger than 16 read the range once per
- * 16 heads.
+ * query heads of its group (G = Hq / Hkv <= 16) or up to 32 (G > 16);
+ * groups larger than 32 read the range once per 32 heads.
  */
 fa_status fa_decode_splitkv_gqa(const void* q, const void* kcache, const void* vcache, void* o,
                                 float* lse, int B, int Hq, int Hkv, int Lkv, int d,

@@ -12,10 +12,14 @@ import exact_attention_116_amd as fa
 
 
 class Fake:
-    """Just enough of a device tensor for the binding's checks."""
+    """Just enough of a device tensor for the binding's checks.  The dtype
+    defaults to the usual one of its element size (bf16, fp32, uint8)."""
 
-    def __init__(self, numel, elem=2):
+    DEFAULT = {1: "torch.uint8", 2: "torch.bfloat16", 4: "torch.float32"}
+
+    def __init__(self, numel, elem=2, dtype=None):
         self._n, self._e = numel, elem
+        self.dtype = dtype or self.DEFAULT[elem]
         self.is_cuda = True
 
     def is_contiguous(self):
@@ -80,7 +84,7 @@ def test_decode_sizes():
     raises_short("workspace", fa.fa_decode_splitkv_gqa, q(), c(), c(), q(), None, B, Hq, Hkv, L, d,
                  4, 0.1, workspace=Fake(100, 1), workspace_bytes=101)
     raises_short("seqlens_k", fa.fa_decode_splitkv_varlen, q(), c(), c(), q(), None,
-                 Fake(B - 1, 4), B, Hq, Hkv, L, d, 4, 0.1)
+                 Fake(B - 1, 4, "torch.int32"), B, Hq, Hkv, L, d, 4, 0.1)
     H = 4
     raises_short("vcache", fa.fa_decode_splitkv, Fake(B * H * d), Fake(B * H * L * d),
                  Fake(B * H * L * d - 1), Fake(B * H * d), B, H, L, d, 8)
@@ -88,11 +92,12 @@ def test_decode_sizes():
 
 def test_varlen_and_quantize_and_backward_sizes():
     B, H, d, tq, tk = 3, 2, 64, 50, 70
+    cu = lambda n: Fake(n, 4, "torch.int32")
     raises_short("cu_seqlens_k", fa.fa_fwd_varlen, Fake(tq * H * d), Fake(tk * H * d),
-                 Fake(tk * H * d), Fake(tq * H * d), Fake(H * tq, 4), Fake(B + 1, 4), Fake(B, 4),
+                 Fake(tk * H * d), Fake(tq * H * d), Fake(H * tq, 4), cu(B + 1), cu(B),
                  B, H, 30, 40, tq, tk, d, 0.1, True)
     raises_short("k", fa.fa_fwd_varlen, Fake(tq * H * d), Fake(tq * H * d), Fake(tk * H * d),
-                 Fake(tq * H * d), Fake(H * tq, 4), Fake(B + 1, 4), Fake(B + 1, 4),
+                 Fake(tq * H * d), Fake(H * tq, 4), cu(B + 1), cu(B + 1),
                  B, H, 30, 40, tq, tk, d, 0.1, True)
     N = 130
     raises_short("scales", fa.fa_fp8_quantize, Fake(B * H * N * d), Fake(d, 4), Fake(B * H * N * d, 1),
@@ -102,5 +107,50 @@ def test_varlen_and_quantize_and_backward_sizes():
     t = lambda: Fake(B * H * N * d)
     raises_short("dk", fa.fa_bwd, t(), t(), t(), t(), t(), Fake(B * H * N, 4), t(),
                  Fake(B * H * N * d - 1), t(), B, H, N, d, 0.1, True)
-    raises_short("dout", fa.fa_bwd_ex, t(), t(), t(), t(), Fake(10), Fake(B * H * N, 4), t(), t(), t(),
-                 B, H, N, d, 0.1, True, dtype=fa.FA_FP16)
+    h = lambda: Fake(B * H * N * d, 2, "torch.float16")
+    raises_short("dout", fa.fa_bwd_ex, h(), h(), h(), h(), Fake(10, 2, "torch.float16"),
+                 Fake(B * H * N, 4), h(), h(), h(), B, H, N, d, 0.1, True, dtype=fa.FA_FP16)
+
+
+def raises_dtype(name, fn, *args, **kw):
+    with pytest.raises(fa.FaError) as e:
+        fn(*args, **kw)
+    assert e.value.status == fa.FA_ERR_INVALID_ARG
+    assert str(e.value).startswith(f"{name} has dtype"), str(e.value)
+
+
+def test_dtypes_are_checked():
+    """A tensor of another element type but enough bytes is refused: its bits
+    would otherwise be read as the stated type."""
+    B, H, N, d = 1, 2, 64, 64
+    full, rows = B * H * N * d, B * H * N
+    ok = lambda: Fake(full)
+    f32 = lambda n: Fake(n, 4)
+    # a float32 q (twice the bytes) and a bf16 lse (enough bytes at double count)
+    raises_dtype("q", fa.fa_fwd, f32(full), ok(), ok(), ok(), f32(rows), B, H, N, d, 0.1, True)
+    raises_dtype("lse", fa.fa_fwd, ok(), ok(), ok(), ok(), Fake(2 * rows, 2), B, H, N, d, 0.1, True)
+    # fp16 inputs with a bf16 v; fp32 output asked for with a bf16 o
+    h = lambda: Fake(full, 2, "torch.float16")
+    raises_dtype("v", fa.fa_fwd_ex, h(), h(), ok(), h(), f32(rows), B, H, N, d, 0.1, True,
+                 in_dtype=fa.FA_FP16, out_dtype=fa.FA_FP16)
+    raises_dtype("o", fa.fa_fwd_ex, ok(), ok(), ok(), Fake(2 * full, 2), f32(rows), B, H, N, d, 0.1,
+                 True, out_dtype=fa.FA_FP32)
+    # fp8 codes may be uint8, int8 or float8_e4m3fn; scales must be fp32
+    nsb = B * H * ((N + 63) // 64)
+    for codes_dt in ("torch.uint8", "torch.int8", "torch.float8_e4m3fn"):
+        c = lambda: Fake(full, 1, codes_dt)
+        raises_dtype("v_scale", fa.fa_fwd_ex, c(), c(), c(), ok(), f32(rows), B, H, N, d, 0.1, True,
+                     in_dtype=fa.FA_FP8_E4M3, q_scale=f32(nsb), k_scale=f32(nsb),
+                     v_scale=Fake(2 * nsb, 2))
+    # int32 lengths for the packed and per-sequence calls
+    raises_dtype("cu_seqlens_q", fa.fa_fwd_varlen, ok(), ok(), ok(), ok(), f32(rows),
+                 f32(B + 1), Fake(B + 1, 4, "torch.int32"), B, H, N, N, N, N, d, 0.1, True)
+    raises_dtype("seqlens_k", fa.fa_decode_splitkv_varlen, Fake(H * d), Fake(H * 10 * d),
+                 Fake(H * 10 * d), Fake(H * d), None, f32(B), B, H, H, 10, d, 2, 0.1)
+    # the decode cache and the backward tensors
+    raises_dtype("kcache", fa.fa_decode_splitkv_gqa, Fake(H * d), Fake(H * 10 * d, 2, "torch.float16"),
+                 Fake(H * 10 * d), Fake(H * d), None, B, H, H, 10, d, 2, 0.1)
+    t = lambda: Fake(full)
+    raises_dtype("dq", fa.fa_bwd, t(), t(), t(), t(), t(), f32(rows), f32(full), t(), t(),
+                 B, H, N, d, 0.1, True)
+    raises_dtype("codes", fa.fa_fp8_quantize, t(), f32(d), Fake(full, 2), f32(nsb), B, H, N, d)
