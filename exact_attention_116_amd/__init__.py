@@ -14,9 +14,11 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
 FA_BF16, FA_FP32, FA_FP8_E4M3, FA_FP16 = range(4)
+FA_DECODE_SCRATCH_BYTES = 32 << 20   # the fixed scratch of fa_decode_splitkv_noalloc
 
 EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_decode_splitkv", "fa_decode_workspace_bytes",
-           "fa_decode_splitkv_ex", "fa_decode_splitkv_gqa", "fa_decode_splitkv_varlen",
+           "fa_decode_splitkv_ex", "fa_decode_splitkv_noalloc", "fa_decode_splitkv_gqa",
+           "fa_decode_splitkv_varlen",
            "fa_fwd_varlen", "fa_fp8_quantize",
            "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_ex",
            "fa_status_string", "fa_last_error")
@@ -61,6 +63,8 @@ def load(path: str | None = None):
     lib.fa_decode_workspace_bytes.restype = Z
     lib.fa_decode_splitkv_ex.argtypes = [P, P, P, P, P, I, I, I, I, I, F, P, Z, P]
     lib.fa_decode_splitkv_ex.restype = I
+    lib.fa_decode_splitkv_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, F, P]
+    lib.fa_decode_splitkv_noalloc.restype = I
     lib.fa_decode_splitkv_gqa.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, P, Z, P]
     lib.fa_decode_splitkv_gqa.restype = I
     lib.fa_decode_splitkv_varlen.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, P, Z, P]
@@ -196,6 +200,19 @@ def fa_decode_splitkv_ex(q, kcache, vcache, o, lse, B, H, Lkv, d, num_splits, sc
                                        float(scale), _ptr(workspace, int(workspace_bytes), "workspace"),
                                        int(workspace_bytes), _stream(stream)),
            "fa_decode_splitkv_ex")
+
+
+def fa_decode_splitkv_noalloc(q, kcache, vcache, o, lse, B, H, Lkv, d, num_splits, scale,
+                              stream=None):
+    """fa_decode_splitkv_ex without a workspace: the partials go to the
+    library's fixed scratch (at most FA_DECODE_SCRATCH_BYTES), so the call
+    allocates nothing.  Calls that overlap on one GPU share that scratch."""
+    t, c = 2 * _n(B, H, d), 2 * _n(B, H, Lkv, d)
+    _check(load().fa_decode_splitkv_noalloc(_ptr(q, t, "q", BF16), _ptr(kcache, c, "kcache", BF16),
+                                            _ptr(vcache, c, "vcache", BF16), _ptr(o, t, "o", BF16),
+                                            _ptr(lse, 4 * _n(B, H), "lse", F32), B, H, Lkv, d,
+                                            num_splits, float(scale), _stream(stream)),
+           "fa_decode_splitkv_noalloc")
 
 
 def fa_decode_splitkv_gqa(q, kcache, vcache, o, lse, B, Hq, Hkv, Lkv, d, num_splits, scale,

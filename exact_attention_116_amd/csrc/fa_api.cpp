@@ -14,6 +14,9 @@
 #include "../../include/fa.h"
 #include "fa_internal.h"
 
+static_assert(fa::kDecodeScratchBytes == (size_t)FA_DECODE_SCRATCH_BYTES,
+              "the fixed decode scratch has the size fa.h states");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -257,6 +260,22 @@ fa_status fa_decode_splitkv(const void* q, const void* kcache, const void* vcach
   st = owned_workspace(decode_ws_bytes(B, H, d, num_splits), &ws, ws_lock);
   if (st != FA_OK) return st;
   return run_decode(q, kcache, vcache, o, nullptr, B, H, 0, Lkv, d, num_splits, scale, ws, nullptr);
+}
+
+fa_status fa_decode_splitkv_noalloc(const void* q, const void* kcache, const void* vcache, void* o,
+                                    float* lse, int B, int H, int Lkv, int d, int num_splits,
+                                    float scale, void* stream) {
+  fa_status st = check_decode(q, kcache, vcache, o, B, H, Lkv, d, num_splits, scale);
+  if (st != FA_OK) return st;
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (decode_ws_bytes(B, H, d, num_splits) > (size_t)FA_DECODE_SCRATCH_BYTES)
+    return fail(FA_ERR_WORKSPACE,
+                "B*H*num_splits*(d+1)*4 bytes of partials exceed FA_DECODE_SCRATCH_BYTES (32 MiB)");
+  void* ws = nullptr;
+  hipError_t e = fa::decode_scratch(&ws);
+  if (e != hipSuccess) return hip_fail(e, "fa_decode_splitkv_noalloc scratch lookup");
+  return run_decode(q, kcache, vcache, o, lse, B, H, 0, Lkv, d, num_splits, scale, ws, stream);
 }
 
 fa_status fa_decode_splitkv_gqa(const void* q, const void* kcache, const void* vcache, void* o,

@@ -22,6 +22,8 @@
 #include "fa_device.hpp"
 #include "fa_internal.h"
 
+#include <mutex>
+
 namespace fa {
 
 template <int D, int NW, int U>
@@ -168,6 +170,39 @@ static hipError_t launch_d(const DecodeArgs& a) {
 
 hipError_t launch_decode(const DecodeArgs& a) {
   return a.d == 128 ? launch_d<128>(a) : launch_d<64>(a);
+}
+
+// ---------------------------------------------------------------------------
+// Fixed scratch for the decode entry point that allocates nothing: the split
+// partials live in this file-scope device array (one copy per GPU, held until
+// the process ends) instead of a workspace.  In host code `scratch` names a
+// host-side stand-in, never the device memory: its device address is taken
+// once per device with hipGetSymbolAddress (with that device current) and
+// only that address is handed to kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};   // device address of `scratch`, per device
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode_combine(const DecodeArgs& a) {

@@ -85,4 +85,10 @@ hipError_t launch_decode_gqa(const DecodeArgs& a);
 // the merge of the split partials (shared by both decode paths)
 hipError_t launch_decode_combine(const DecodeArgs& a);
 
+// The library's fixed decode scratch (for the entry point that allocates
+// nothing): its device address on the current device, looked up once per
+// device.  kDecodeScratchBytes is FA_DECODE_SCRATCH_BYTES of fa.h.
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+hipError_t decode_scratch(void** ptr);
+
 }  // namespace fa

@@ -165,6 +165,31 @@ fa_status fa_decode_splitkv_ex(const void* q, const void* kcache, const void* vc
                                void* stream);
 
 /*
+ * fa_decode_splitkv_noalloc -- fa_decode_splitkv_ex for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels and arguments, with the
+ * split partials kept in a fixed scratch array inside the library instead of
+ * a workspace.  The call makes no hipMalloc/hipFree and no host allocation
+ * on its success path.
+ *
+ * Limit: the partials, fa_decode_workspace_bytes(B, H, d, num_splits) =
+ * B*H*num_splits*(d+1)*4 bytes rounded up to 256, must fit in
+ * FA_DECODE_SCRATCH_BYTES (32 MiB; e.g. B=8, H=32, d=128 up to 254 splits),
+ * else FA_ERR_WORKSPACE and nothing is launched.  Each GPU the library runs
+ * on holds its own copy of the scratch until the process ends; the first
+ * call on a device looks up its address there.  Every call on one GPU
+ * shares that GPU's scratch, so calls that overlap on one GPU (concurrent
+ * streams, several host threads without ordering) race and give wrong
+ * results: serialise them, e.g. on one stream.  Nothing in the scratch
+ * needs clearing: each call writes every partial it reads.
+ * Other arguments, layouts and errors as fa_decode_splitkv_ex.
+ */
+#define FA_DECODE_SCRATCH_BYTES (32u << 20)
+fa_status fa_decode_splitkv_noalloc(const void* q, const void* kcache, const void* vcache, void* o,
+                                    float* lse, int B, int H, int Lkv, int d, int num_splits,
+                                    float scale, void* stream);
+
+/*
  * fa_decode_splitkv_gqa -- single-query split-KV decode where several query
  * heads share one key/value head (grouped-query attention; multi-query
  * attention when Hkv = 1: the MQA note among the related posts of the CSDN

@@ -131,6 +131,36 @@ def test_decode_ex_rejects(lib, kw, status):
     assert st == status
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(o=A + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=A + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(S=0), fa.FA_ERR_INVALID_ARG),
+    (dict(S=300, Lkv=200), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    # partials of 8*32*255*129*4 bytes: just past the 32 MiB scratch
+    (dict(B=8, H=32, S=255, Lkv=65536), fa.FA_ERR_WORKSPACE),
+    (dict(B=1024, H=64, S=1, Lkv=16), fa.FA_ERR_WORKSPACE),
+])
+def test_decode_noalloc_rejects(lib, kw, status):
+    a = dict(q=A, kc=A, vc=A, o=A, lse=None, B=1, H=2, Lkv=16, d=128, S=4, scale=0.1)
+    a.update(kw)
+    st = lib.fa_decode_splitkv_noalloc(a["q"], a["kc"], a["vc"], a["o"], a["lse"], a["B"], a["H"],
+                                       a["Lkv"], a["d"], a["S"], a["scale"], None)
+    assert st == status
+    assert fa.fa_last_error() != ""
+
+
+def test_decode_noalloc_limit_matches_header():
+    with open(os.path.join(ROOT, "include", "fa.h")) as f:
+        m = re.search(r"#define FA_DECODE_SCRATCH_BYTES \((\d+)u << (\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.FA_DECODE_SCRATCH_BYTES == 32 << 20
+    # the largest C4-shaped call that fits: 8 x 32 heads, d = 128, 254 splits
+    assert fa.fa_decode_workspace_bytes(8, 32, 128, 254) <= fa.FA_DECODE_SCRATCH_BYTES
+    assert fa.fa_decode_workspace_bytes(8, 32, 128, 255) > fa.FA_DECODE_SCRATCH_BYTES
+
+
 def test_decode_rejects(lib):
     assert lib.fa_decode_splitkv(A, A, A, None, 1, 1, 16, 128, 4) == fa.FA_ERR_INVALID_ARG
     assert lib.fa_decode_splitkv(A, A, A, A, 1, 1, 16, 128, 32) == fa.FA_ERR_INVALID_ARG
