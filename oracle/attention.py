@@ -187,6 +187,51 @@ def attention_backward(q, k, v, do, scale, causal=False, row_block=ROW_BLOCK):
             dV.reshape(lead + vf.shape[-2:]))
 
 
+def attention_backward_rows(q_rows, qidx, k, v, do_rows, scale, causal=False):
+    """dQ for selected query rows of one (batch, head): the query-side
+    gradient of a row needs only that row's scores, probabilities and dO.
+
+    q_rows, do_rows: [r, d] (rows ``qidx``); k, v: [Nk, d].  Returns dQ [r, d].
+    """
+    q_rows, k, v, do_rows = (np.asarray(x, np.float64) for x in (q_rows, k, v, do_rows))
+    dq, _, _ = _backward_rows(q_rows, k, v, do_rows, scale, causal, np.asarray(qidx, np.int64))
+    return dq
+
+
+def attention_backward_keys(q, k, v, do, kidx, scale, causal=False, row_block=ROW_BLOCK):
+    """dK and dV for selected key rows ``kidx`` of one (batch, head).
+
+    Key j's gradients sum over every query row i that sees it:
+        dV_j = sum_i P_ij dO_i,   dK_j = scale * sum_i dS_ij q_i,
+        dS_ij = P_ij (dP_ij - sum_j' P_ij' dP_ij'),  dP_ij = dO_i . v_j,
+    so each query row still needs its full scores (for its max and sum) and
+    its full dP (for the row term), but only the columns ``kidx`` of P and
+    dS enter the sums.  q, do: [N, d]; k, v: [Nk, d].  Returns
+    (dK [len(kidx), d], dV [len(kidx), d]).
+    """
+    q, k, v, do = (np.asarray(x, np.float64) for x in (q, k, v, do))
+    kidx = np.asarray(kidx, np.int64)
+    dK = np.zeros((kidx.size, k.shape[1]))
+    dV = np.zeros((kidx.size, v.shape[1]))
+    N = q.shape[0]
+    for r0 in range(0, N, row_block):
+        idx = np.arange(r0, min(r0 + row_block, N))
+        S = scale * (q[idx] @ k.T)
+        if causal:
+            j = np.arange(k.shape[0])
+            S = np.where(j[None, :] <= idx[:, None], S, -np.inf)
+        m = S.max(axis=1)
+        E = np.exp(S - m[:, None])
+        P = E / E.sum(axis=1)[:, None]
+        dP = do[idx] @ v.T
+        row_term = (P * dP).sum(axis=1)
+        Pc = P[:, kidx]
+        dSc = Pc * (dP[:, kidx] - row_term[:, None])
+        dV += Pc.T @ do[idx]
+        dK += scale * (dSc.T @ q[idx])
+    return dK, dV
+
+
 # ---------------------------------------------------------------------------
 # Split-KV (Flash-Decoding): partial results per key range, then the merge
 # ---------------------------------------------------------------------------

@@ -547,6 +547,46 @@ def test_backward_invariants(causal):
         np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_selected_rows_and_keys_against_torch(causal):
+    """dQ of selected query rows and dK, dV of selected key rows equal those
+    rows of torch's float64 autograd through SDPA, with row blocks smaller
+    than the sequence so that the key-side sums cross blocks."""
+    rng = np.random.default_rng(81 + causal)
+    N, d, scale = 97, 16, 0.35
+    q, k, v, do = (_rand(rng, N, d) for _ in range(4))
+    tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_() for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)
+    out.backward(torch.from_numpy(do))
+    rows = np.array([0, 1, 31, 32, 50, 96])
+    dq = oracle.attention_backward_rows(q[rows], rows, k, v, do[rows], scale, causal)
+    np.testing.assert_allclose(dq, tq.grad.numpy()[rows], rtol=0, atol=1e-12)
+    keys = np.array([0, 5, 63, 64, 95, 96])
+    dk, dv = oracle.attention_backward_keys(q, k, v, do, keys, scale, causal, row_block=20)
+    np.testing.assert_allclose(dk, tk.grad.numpy()[keys], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy()[keys], rtol=0, atol=1e-12)
+    # and the same rows of the full oracle gradients
+    dQ, dK, dV = oracle.attention_backward(q, k, v, do, scale, causal)
+    np.testing.assert_allclose(dq, dQ[rows], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dk, dK[keys], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dv, dV[keys], rtol=0, atol=1e-13)
+
+
+def test_backward_keys_last_key_closed_form():
+    """With causal masking the last key is seen by the last query only:
+    dV_last = P_last,last dO_last, and dK_last = scale P (dP - sum P dP) q."""
+    rng = np.random.default_rng(83)
+    N, d, scale = 40, 8, 0.5
+    q, k, v, do = (_rand(rng, N, d) for _ in range(4))
+    dk, dv = oracle.attention_backward_keys(q, k, v, do, [N - 1], scale, True, row_block=7)
+    s = scale * (q[-1] @ k.T)
+    p = np.exp(s - s.max())
+    p /= p.sum()
+    dp = v @ do[-1]
+    np.testing.assert_allclose(dv[0], p[-1] * do[-1], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dk[0], scale * p[-1] * (dp[-1] - p @ dp) * q[-1], rtol=1e-11, atol=1e-14)
+
+
 # ---------------------------------------------------------------------------
 # ragged batches (packed sequences, unequal query/key lengths)
 # ---------------------------------------------------------------------------
