@@ -25,8 +25,41 @@ def u8_to_dev(codes: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(codes)).cuda()
 
 
+_BF16_TABLE = None
+
+
+def bf16_values(bits: np.ndarray) -> np.ndarray:
+    """float64 values of bf16 bit patterns: the oracle's decoder applied once
+    to all 65536 codes, then looked up (the same values, fast enough for the
+    full-size workloads)."""
+    global _BF16_TABLE
+    if _BF16_TABLE is None:
+        _BF16_TABLE = oracle.decode_bf16(np.arange(65536, dtype=np.uint16))
+    return _BF16_TABLE[np.asarray(bits, dtype=np.uint16)]
+
+
+class ErrStats:
+    """Running max-abs, mean-abs and max LSE relative error over a whole
+    configuration, for one summary line per configuration."""
+
+    def __init__(self, name):
+        self.name, self.max, self.sum, self.n, self.lse = name, 0.0, 0.0, 0, 0.0
+
+    def add(self, got, ref, lse_got=None, lse_ref=None):
+        err = np.abs(np.asarray(got, np.float64) - ref)
+        self.max = max(self.max, float(err.max()))
+        self.sum += float(err.sum())
+        self.n += err.size
+        if lse_got is not None:
+            self.lse = max(self.lse, float(lse_rel(lse_got, lse_ref).max()))
+
+    def report(self):
+        print(f"[config {self.name}] max_abs={self.max:.3e} mean_abs={self.sum / max(self.n, 1):.3e} "
+              f"lse_rel={self.lse:.3e} over {self.n} outputs", flush=True)
+
+
 def dev_bf16_to_f64(t: torch.Tensor) -> np.ndarray:
-    return oracle.decode_bf16(t.detach().cpu().view(torch.int16).numpy().view(np.uint16))
+    return bf16_values(t.detach().cpu().view(torch.int16).numpy().view(np.uint16))
 
 
 def dev_to_f64(t: torch.Tensor) -> np.ndarray:

@@ -15,7 +15,7 @@ import torch
 
 import fa_inputs as fi
 import oracle
-from _gpu_util import bf16_to_dev, dev_to_f64, say
+from _gpu_util import bf16_to_dev, bf16_values, dev_to_f64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -43,8 +43,11 @@ def run(fa, q, k, v, do, B, H, N, d, scale, causal, own_ws=False):
     return dq, dk, dv
 
 
-def check(got, ref, what):
-    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+def check(got, ref, what, names=("dQ", "dK", "dV")):
+    """Gates per gradient tensor; returns each one's mean-abs error relative
+    to its mean |ref|."""
+    rel = []
+    for name, g, r in zip(names, got, ref):
         g = dev_to_f64(g) if isinstance(g, torch.Tensor) else g
         assert np.all(np.isfinite(g)), f"{what} {name}: non-finite"
         err = np.abs(g - r)
@@ -55,6 +58,8 @@ def check(got, ref, what):
               f"mean_abs={err.mean():.3e} (rel {rmean:.2e}) |ref|max={amax:.3e}", flush=True)
         assert err.max() <= REL_MAX * amax + ABS, f"{what} {name}: max rel {rmax}"
         assert err.mean() <= REL_MEAN * amean + ABS, f"{what} {name}: mean rel {rmean}"
+        rel.append(rmean)
+    return np.array(rel)
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -72,35 +77,61 @@ def test_bwd_edge_shapes(gpu_lib, N, causal, d):
     check(got, ref, f"N={N} d={d} causal={causal}")
 
 
+def tile_edges_and_random(N, tile, n_random, seed):
+    edges = np.r_[np.arange(0, N, tile), np.minimum(np.arange(tile - 1, N + tile - 1, tile), N - 1)]
+    return np.unique(np.r_[edges, np.random.default_rng(seed).choice(N, n_random, replace=False)])
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_llama_layer(gpu_lib, causal):
     """B=2 H=32 N=2048 d=128 (the LLaMA-7B-shaped layer): every element of
-    three sampled (b, h) heads against the oracle."""
+    every (b, h) against the oracle."""
     fa = gpu_lib
     w = fi.WORKLOADS[2]
     say(f"bwd {w.name} causal={causal}: generating")
     qb, kb, vb, dob = gen(w.wid, w.B, w.H, w.N, w.d)
     got = run(fa, *map(bf16_to_dev, (qb, kb, vb, dob)), w.B, w.H, w.N, w.d, w.scale, causal)
     got = [dev_to_f64(x) for x in got]
-    for b, h in [(0, 0), (1, 17), (1, 31)]:
-        ref = oracle.attention_backward(*(oracle.decode_bf16(x[b, h]) for x in (qb, kb, vb, dob)),
-                                        w.scale, causal)
-        check([x[b, h] for x in got], ref, f"(b={b},h={h})")
+    worst = np.zeros(3)
+    for b in range(w.B):
+        for h in range(w.H):
+            ref = oracle.attention_backward(*(bf16_values(x[b, h]) for x in (qb, kb, vb, dob)),
+                                            w.scale, causal)
+            worst = np.maximum(worst, check([x[b, h] for x in got], ref, f"(b={b},h={h})"))
+    say(f"[config backward C2 {'causal' if causal else 'non-causal'}] worst mean-abs error relative "
+        f"to mean |ref| over all 64 heads: dQ {worst[0]:.2e} dK {worst[1]:.2e} dV {worst[2]:.2e}")
 
 
 def test_bwd_long_causal(gpu_lib):
-    """B=1 H=16 N=16384 d=128 causal: every element of one sampled head."""
+    """B=1 H=16 N=16384 d=128 causal, every head: dQ on the first and last
+    row of every 128-query tile plus 512 random rows; dK and dV on the first
+    and last key of every 128-key tile plus 256 random keys."""
+    from concurrent.futures import ThreadPoolExecutor
     fa = gpu_lib
     w = fi.WORKLOADS[3]
     say(f"bwd {w.name}: generating")
     qb, kb, vb, dob = gen(w.wid, w.B, w.H, w.N, w.d)
     got = run(fa, *map(bf16_to_dev, (qb, kb, vb, dob)), w.B, w.H, w.N, w.d, w.scale, True)
-    h = 11
-    got = [dev_to_f64(x[0, h]) for x in got]
-    say("bwd long causal: oracle for head 11")
-    ref = oracle.attention_backward(*(oracle.decode_bf16(x[0, h]) for x in (qb, kb, vb, dob)),
-                                    w.scale, True)
-    check(got, ref, f"(b=0,h={h})")
+    gq, gk, gv = (dev_to_f64(x[0]) for x in got)
+
+    def ref_head(h):
+        q, k, v, do = (bf16_values(x[0, h]) for x in (qb, kb, vb, dob))
+        rows = tile_edges_and_random(w.N, 128, 512, 3700 + h)
+        keys = tile_edges_and_random(w.N, 128, 256, 3800 + h)
+        dq = oracle.attention_backward_rows(q[rows], rows, k, v, do[rows], w.scale, True)
+        dk, dv = oracle.attention_backward_keys(q, k, v, do, keys, w.scale, True)
+        return rows, keys, dq, dk, dv
+
+    say("bwd long causal: oracle for all 16 heads (selected query and key rows)")
+    worst = np.zeros(3)
+    with ThreadPoolExecutor(4) as ex:
+        for h, (rows, keys, dq, dk, dv) in enumerate(ex.map(ref_head, range(w.H))):
+            r = check([gq[h, rows]], [dq], f"h={h} rows={len(rows)}")
+            rk = check([gk[h, keys], gv[h, keys]], [dk, dv], f"h={h} keys={len(keys)}",
+                       names=("dK", "dV"))
+            worst = np.maximum(worst, np.r_[r, rk])
+    say(f"[config backward C3 causal] worst mean-abs error relative to mean |ref| over all 16 "
+        f"heads: dQ {worst[0]:.2e} dK {worst[1]:.2e} dV {worst[2]:.2e}")
 
 
 def test_bwd_library_workspace(gpu_lib):

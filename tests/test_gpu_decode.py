@@ -5,7 +5,7 @@ import torch
 
 import fa_inputs as fi
 import oracle
-from _gpu_util import bf16_to_dev, check_bf16_gates, dev_to_f64, say
+from _gpu_util import ErrStats, bf16_values, bf16_to_dev, check_bf16_gates, dev_to_f64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -74,8 +74,8 @@ def test_decode_default_entry_point(gpu_lib):
 
 
 def test_decode_full_size(gpu_lib):
-    """B=8, H=32, Lkv=65536, d=128, 64 splits; sampled (b,h) against the oracle,
-    every (b,h) against the single-split run of the same kernel pair."""
+    """B=8, H=32, Lkv=65536, d=128, 64 splits: every (b, h) against the
+    oracle.  The one-split run of the same kernels is checked too."""
     fa = gpu_lib
     w = fi.WORKLOADS[4]
     say(f"decode {w.name}: generating 8 GiB of K/V")
@@ -83,15 +83,23 @@ def test_decode_full_size(gpu_lib):
     q, k, v = map(bf16_to_dev, (qb, kb, vb))
     say("decode full size: running")
     o, lse, _, _ = run_ex(fa, q, k, v, w.B, w.H, w.Lkv, w.d, w.num_splits, w.scale)
-    og, lg = dev_to_f64(o), dev_to_f64(lse)
-    assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg))
-    for b, h in [(0, 0), (3, 17), (7, 31)]:
-        Q, K, V = (oracle.decode_bf16(x[b, h]) for x in (qb, kb, vb))
-        O, L = oracle.decode_attention(Q, K, V, w.scale)
-        check_bf16_gates(og[b, h], O, lg[b, h:h + 1], L, f"(b={b},h={h})")
     o1, lse1, _, _ = run_ex(fa, q, k, v, w.B, w.H, w.Lkv, w.d, 1, w.scale)
-    assert np.abs(dev_to_f64(o1) - og).max() <= 1e-2
-    assert np.abs(dev_to_f64(lse1) - lg).max() <= 1e-3
+    og, lg = dev_to_f64(o), dev_to_f64(lse)
+    og1, lg1 = dev_to_f64(o1), dev_to_f64(lse1)
+    assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg))
+    st = ErrStats("C4 decode B=8 H=32 Lkv=65536 S=64")
+    st1 = ErrStats("C4 decode, one split")
+    say("decode full size: oracle for all 256 (b, h)")
+    for b in range(w.B):
+        for h in range(w.H):
+            Q, K, V = (bf16_values(x[b, h]) for x in (qb, kb, vb))
+            O, L = oracle.decode_attention(Q, K, V, w.scale)
+            check_bf16_gates(og[b, h], O, lg[b, h:h + 1], L, f"(b={b},h={h})")
+            check_bf16_gates(og1[b, h], O, lg1[b, h:h + 1], L, f"(b={b},h={h}) one split")
+            st.add(og[b, h], O, lg[b, h:h + 1], L)
+            st1.add(og1[b, h], O, lg1[b, h:h + 1], L)
+    st.report()
+    st1.report()
 
 
 def test_decode_deterministic_and_in_bounds(gpu_lib):
