@@ -52,5 +52,29 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     return LIB
 
 
+ASAN_LIB = os.path.join(BUILD_DIR, "libfa_host_asan.so")
+
+
+def build_host_asan() -> str:
+    """CPU-only build of the C-ABI layer (fa_api.cpp) under AddressSanitizer,
+    linked with host stand-ins for the HIP runtime calls and the kernel
+    launchers (csrc/host_stubs.cpp); no device code.  For the CPU tests of
+    argument validation and workspace handling.  Loading it into Python
+    needs the sanitizer runtime preloaded (``asan_runtime()``)."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    tmp = ASAN_LIB + ".tmp"
+    _run(["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-fsanitize=address",
+          "-fno-omit-frame-pointer", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include",
+          "-I", os.path.join(ROOT, "include"), os.path.join(CSRC, "fa_api.cpp"),
+          os.path.join(CSRC, "host_stubs.cpp"), "-o", tmp])
+    os.replace(tmp, ASAN_LIB)
+    return ASAN_LIB
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's AddressSanitizer runtime (to LD_PRELOAD)."""
+    return _run(["g++", "-print-file-name=libasan.so"]).stdout.strip()
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

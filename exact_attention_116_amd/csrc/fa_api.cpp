@@ -1,6 +1,6 @@
 // C-ABI host layer of the attention library: argument validation, the
-// library-owned workspace (decode partials, backward row sums) and dispatch
-// to the HIP launchers.
+// library-owned workspace (decode partials, backward row sums; released when
+// the library is unloaded) and dispatch to the HIP launchers.
 // Every check runs before any HIP call, so a rejected call touches no device.
 #include <hip/hip_runtime_api.h>
 
@@ -143,11 +143,22 @@ fa_status run_decode(const void* q, const void* kc, const void* vc, void* o, flo
 }
 
 // Library-owned decode workspace: one buffer per device, grown on demand and
-// kept until the process ends.
+// released when the library is unloaded (dlclose, or the end of the process).
 struct OwnedWorkspace {
   std::mutex mu;
   std::vector<void*> ptr;
   std::vector<size_t> bytes;
+  ~OwnedWorkspace() {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) cur = -1;
+    for (size_t d = 0; d < ptr.size(); ++d) {
+      if (!ptr[d]) continue;
+      (void)hipSetDevice((int)d);   // free each buffer with its own device current
+      (void)hipFree(ptr[d]);
+      ptr[d] = nullptr;
+    }
+    if (cur >= 0) (void)hipSetDevice(cur);
+  }
 };
 OwnedWorkspace g_ws;
 
