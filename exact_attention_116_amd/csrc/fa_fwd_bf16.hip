@@ -37,6 +37,9 @@
 //    leaves the result exact and skips most rescales.  l sums the fp32
 //    probabilities (before their bf16 rounding for the MFMA), so the stored
 //    log-sum-exp carries no bf16 error even for rows with few keys.
+//  * The epilogue stages each wave's 32 output rows in LDS and stores them
+//    as whole rows (16 lanes per 256-byte row), not 8 bytes per row and
+//    lane.
 //  * Causal: key tiles entirely above the diagonal are never loaded; within
 //    a workgroup, a wave whose 32 queries all precede a tile skips its math;
 //    masking is applied only on tiles that straddle the diagonal or N.
@@ -320,24 +323,45 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // query that saw no key) ----
   l = sum_pair32(l);
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  if (my_q < Lq) {
-    const size_t orow = qbase + (size_t)my_q * rs;
+  if constexpr (OUT_F32) {
+    if (my_q < Lq) {
+      const size_t orow = qbase + (size_t)my_q * rs;
+#pragma unroll
+      for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int d0 = 32 * cb + 8 * ii + 4 * g;
+          *reinterpret_cast<f32x4*>(static_cast<float*>(o) + orow + d0) =
+              f32x4{acc[cb][4 * ii] * inv, acc[cb][4 * ii + 1] * inv, acc[cb][4 * ii + 2] * inv,
+                    acc[cb][4 * ii + 3] * inv};
+        }
+    }
+  } else {
+    // 16-bit output: each wave stages its 32 rows in LDS (free after the
+    // last tile's barrier), 16-byte chunks XOR-swizzled by row, and reads
+    // them back so that 16 lanes store one whole row: every store
+    // instruction writes 64 x 16 contiguous bytes per row group instead of
+    // 8 bytes in each of 32 rows.
+    uint8_t* Os = reinterpret_cast<uint8_t*>(smem) + wave * 32 * RB;
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const int d0 = 32 * cb + 8 * ii + 4 * g;
-        const float o0 = acc[cb][4 * ii] * inv, o1 = acc[cb][4 * ii + 1] * inv;
-        const float o2 = acc[cb][4 * ii + 2] * inv, o3 = acc[cb][4 * ii + 3] * inv;
-        if constexpr (OUT_F32) {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(o) + orow + d0) = f32x4{o0, o1, o2, o3};
-        } else {
-          *reinterpret_cast<u32x2*>(static_cast<bf16*>(o) + orow + d0) =
-              u32x2{pack16<F16>(o0, o1), pack16<F16>(o2, o3)};
-        }
+        const int c = 4 * cb + ii;
+        *reinterpret_cast<u32x2*>(Os + l32 * RB + 16 * (c ^ (l32 % NCH)) + 8 * g) =
+            u32x2{pack16<F16>(acc[cb][4 * ii] * inv, acc[cb][4 * ii + 1] * inv),
+                  pack16<F16>(acc[cb][4 * ii + 2] * inv, acc[cb][4 * ii + 3] * inv)};
       }
-    if (g == 0) lse[lbase + my_q] = l > 0.f ? (m + __builtin_amdgcn_logf(l)) * kLn2 : kNegInf;
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's rows are in LDS
+#pragma unroll
+    for (int k = 0; k < 32 * NCH / 64; ++k) {
+      const int L = 64 * k + lane, r = L / NCH, ch = L % NCH;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(Os + r * RB + 16 * (ch ^ (r % NCH)));
+      if (qw + r < Lq)
+        *reinterpret_cast<u32x4*>(static_cast<bf16*>(o) + qbase + (size_t)(qw + r) * rs + 8 * ch) = val;
+    }
   }
+  if (my_q < Lq && g == 0) lse[lbase + my_q] = l > 0.f ? (m + __builtin_amdgcn_logf(l)) * kLn2 : kNegInf;
 }
 
 template <int D, int BC, int NW, bool CAUSAL, bool OUT_F32, bool F16>

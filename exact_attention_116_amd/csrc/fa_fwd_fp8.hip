@@ -368,19 +368,33 @@ void fa_fwd_fp8_dl_kernel(const uint8_t* __restrict__ q, const uint8_t* __restri
   l = sum_pair32(l);
   // acc holds 256 * sum_t (r_t / r_last) sum_j p_j code_j 2^(e_t - e_max)
   const float fac = __builtin_amdgcn_ldexpf(r_cur, e_max) / l;
-  if (my_q < N) {
-    const size_t row = (size_t)bh * N + my_q;
+  // Each wave stages its 32 bf16 output rows in LDS (free after the last
+  // tile's barrier), 16-byte chunks XOR-swizzled by row, and stores them
+  // back as whole 256-byte rows, 16 lanes per row.
+  {
+    constexpr int ORB = D * 2;             // bytes per bf16 output row
+    constexpr int OCH = ORB / 16;          // 16-byte chunks per row
+    uint8_t* Os = smem + wave * 32 * ORB;
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const int d0 = 32 * cb + 8 * ii + 4 * g;
-        const float o0 = acc[cb][4 * ii] * fac, o1 = acc[cb][4 * ii + 1] * fac;
-        const float o2 = acc[cb][4 * ii + 2] * fac, o3 = acc[cb][4 * ii + 3] * fac;
-        *reinterpret_cast<u32x2*>(o + row * D + d0) = u32x2{pack_bf16(o0, o1), pack_bf16(o2, o3)};
+        const int ch = 4 * cb + ii;
+        *reinterpret_cast<u32x2*>(Os + l32 * ORB + 16 * (ch ^ (l32 % OCH)) + 8 * g) =
+            u32x2{pack_bf16(acc[cb][4 * ii] * fac, acc[cb][4 * ii + 1] * fac),
+                  pack_bf16(acc[cb][4 * ii + 2] * fac, acc[cb][4 * ii + 3] * fac)};
       }
-    if (g == 0) lse[row] = (m + __builtin_amdgcn_logf(l) - kLog2PScale) * kLn2;
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's rows are in LDS
+#pragma unroll
+    for (int k = 0; k < 32 * OCH / 64; ++k) {
+      const int L = 64 * k + lane, r = L / OCH, ch = L % OCH;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(Os + r * ORB + 16 * (ch ^ (r % OCH)));
+      if (qw + r < N)
+        *reinterpret_cast<u32x4*>(o + ((size_t)bh * N + qw + r) * D + 8 * ch) = val;
+    }
   }
+  if (my_q < N && g == 0)
+    lse[(size_t)bh * N + my_q] = (m + __builtin_amdgcn_logf(l) - kLog2PScale) * kLn2;
 }
 
 template <int NW2>
