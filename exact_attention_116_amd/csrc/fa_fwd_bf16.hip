@@ -32,9 +32,12 @@
 //    consecutive keys -- the order in which the score accumulator hands P^T
 //    to the next MFMA.  Operand reads run four MFMAs ahead of their use.
 //  * Softmax runs in base 2 with scale*log2(e) folded into one FMA.  The
-//    reference max is only moved (and O, l rescaled) when some lane's max
-//    grows by more than 2^8; otherwise the stale reference is kept, which
-//    leaves the result exact and skips most rescales.  l sums the fp32
+//    reference max is only moved (and O, l rescaled) when a tile's weights
+//    against it sum to 2^8 or more on some lane, which includes every tile
+//    where a lane's max grows by more than 2^8; otherwise the stale
+//    reference is kept, which leaves the result exact and skips most
+//    rescales.  A tile's own max is only taken in those tiles, after its
+//    weights were formed against the stale reference.  l sums the fp32
 //    probabilities (before their bf16 rounding for the MFMA), so the stored
 //    log-sum-exp carries no bf16 error even for rows with few keys.
 //  * The epilogue stages each wave's 32 output rows in LDS and stores them
@@ -45,7 +48,7 @@
 //    masking is applied only on tiles that straddle the diagonal or N.
 //  * IEEE fp16 inputs (F16) take the same path with the fp16 MFMA: the
 //    layouts, swizzles and transposing reads only see 16-bit elements.  P is
-//    then rounded to fp16 (at most 2^8 under the lazy rescale, so in range;
+//    then rounded to fp16 (below 2^8 under the lazy rescale, so in range;
 //    terms below 2^-24 of the reference are lost from P*V but not from l)
 //    and O is stored as fp16 unless fp32 output is asked for.
 //  * Packed batches of unequal lengths use the same kernel with runtime
@@ -254,38 +257,48 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       }
 
       // ---- online softmax (base 2) ----
-      float mx = kNegInf;
+      // The tile is exponentiated against the reference max m without first
+      // taking its own max.  Its weights may then exceed 1 (exact in fp32
+      // and bf16); a tile whose weights sum to 2^8 or more on some lane
+      // (any weight above 2^8 among them, i.e. a max that grew by more than
+      // 8 in base 2), or a lane with no reference yet, takes the tile max,
+      // moves the reference there (O and l rescaled) and forms its weights
+      // again.  So the reference moves at least whenever the max-based lazy
+      // rule would move it, and the max over every score of a tile is taken
+      // only in those rare tiles.
+      const float l_in = l;
+      bf16x8 pb[BC / 16];
+      auto form_p = [&](float mref) __attribute__((always_inline)) {
 #pragma unroll
-      for (int b = 0; b < BC / 32; ++b)
+        for (int t = 0; t < BC / 16; ++t) {
+          uint32_t w[4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[b][i]);
-      mx = max_pair32(mx) * c;
-      const float m_cand = fmaxf(m, mx);
-      // move the reference max only when it would grow by more than 2^8
-      if (__builtin_amdgcn_ballot_w64(m_cand > m + 8.f)) {
+          for (int h = 0; h < 4; ++h) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[t >> 1][8 * (t & 1) + 2 * h], c, -mref));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[t >> 1][8 * (t & 1) + 2 * h + 1], c, -mref));
+            w[h] = pack16<F16>(p0, p1);
+            l += p0 + p1;
+          }
+          pb[t] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+        }
+      };
+      form_p(m == kNegInf ? 0.f : m);
+      if (__builtin_amdgcn_ballot_w64(!(l - l_in < 256.f) || m == kNegInf)) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int b = 0; b < BC / 32; ++b)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[b][i]);
+        mx = max_pair32(mx) * c;
+        const float m_cand = fmaxf(m, mx);
         const float alpha = (m_cand == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m - m_cand);
         m = m_cand;
-        l *= alpha;
 #pragma unroll
         for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) acc[cb][i] *= alpha;
-      }
-      const float mref = (m == kNegInf) ? 0.f : m;
-
-      // P^T in bf16, grouped as the B operands of the 16-key MFMA steps
-      bf16x8 pb[BC / 16];
-#pragma unroll
-      for (int t = 0; t < BC / 16; ++t) {
-        uint32_t w[4];
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[t >> 1][8 * (t & 1) + 2 * h], c, -mref));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[t >> 1][8 * (t & 1) + 2 * h + 1], c, -mref));
-          w[h] = pack16<F16>(p0, p1);
-          l += p0 + p1;
-        }
-        pb[t] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+        l = l_in * alpha;
+        form_p(m == kNegInf ? 0.f : m);
       }
 
       // ---- O^T += V^T * P^T ----
