@@ -89,6 +89,17 @@ def traffic_bytes(workload):
     return 1024.0 * (t["fetch_kib"] * COUNTER_SCALE["fetch"] + t["write_kib"] * COUNTER_SCALE["write"])
 
 
+def traffic_source(workload):
+    """Where a ``traffic`` figure comes from: it is not measured by this run."""
+    t = TRAFFIC_KIB.get(workload)
+    if t is None:
+        return None
+    state = "current" if traffic_bytes(workload) is not None else "stale: kernel source changed, traffic null"
+    return (f"stored rocprofv3 FETCH_SIZE/WRITE_SIZE counters of an earlier run "
+            f"(profiles/hbm_traffic_counters.md), for sources {'+'.join(t['src'])} + fa_device.hpp "
+            f"with sha256 {t['sha256'][:16]}...; {state}")
+
+
 def fwd_flops(w, causal):
     f = 4.0 * w.B * w.H * w.N * w.N * w.d
     return f / 2 if causal else f
@@ -408,6 +419,28 @@ def main():
     wall = time.perf_counter() - wall0
     ms_step = t_all0.elapsed_time(t_all1) / args.steps
 
+    # C3 back to back: K launches under one event pair, with no other
+    # workload between them (inside a step the memory-bound decode launches
+    # let the clock recover between the heavy ones)
+    steady = None
+    c3_job = next((j for j in jobs if j[0] == "c3"), None)
+    if c3_job is not None:
+        n_steady = max(20, args.steps)
+        for _ in range(3):
+            c3_job[1]()
+        s0 = torch.cuda.Event(enable_timing=True)
+        s1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s0.record(stream)
+        for _ in range(n_steady):
+            c3_job[1]()
+        s1.record(stream)
+        torch.cuda.synchronize()
+        ms = s0.elapsed_time(s1) / n_steady
+        a = c3_job[2] / (ms * 1e-3) / 1e12
+        steady = {"launches": n_steady, "ms_mean": ms, "achieved": a, "peak": PEAK_BF16_TFLOPS,
+                  "unit": "TFLOP/s", "frac": a / PEAK_BF16_TFLOPS}
+
     res = {}
     for i, (name, _, flops, nbytes, kind) in enumerate(jobs):
         ts = np.array([evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)])
@@ -430,7 +463,10 @@ def main():
         a = res[dom]["tflops"]
         roof = {"kernel": f"fa_fwd_bf16_kernel ({dom})", "bound": "mfma", "achieved": a,
                 "peak": pk, "unit": "TFLOP/s", "frac": a / pk, "traffic": traffic_bytes(dom),
+                "traffic_source": traffic_source(dom),
                 "algorithmic_bytes": res[dom]["bytes"]}
+        if dom == "c3" and steady is not None:
+            roof["steady"] = steady
     decode = None
     if "c4" in res:
         g = res["c4"]["gbs"]
@@ -447,6 +483,7 @@ def main():
                                "bound": "hbm", "achieved": g, "peak": PEAK_HBM_GBS,
                                "unit": "GB/s", "frac": g / PEAK_HBM_GBS,
                                "traffic": traffic_bytes("c4"),
+                               "traffic_source": traffic_source("c4"),
                                "algorithmic_bytes": res["c4"]["bytes"]}}
     decode_gqa = {}
     for tag in ("c6", "c7"):
@@ -461,6 +498,7 @@ def main():
                                             "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                             "frac": g / PEAK_HBM_GBS,
                                             "traffic": traffic_bytes(tag),
+                                            "traffic_source": traffic_source(tag),
                                             "algorithmic_bytes": res[tag]["bytes"]}}
     varlen = None
     if "c8" in res:
