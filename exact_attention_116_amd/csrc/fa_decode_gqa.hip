@@ -113,11 +113,16 @@ void fa_decode_gqa_split_kernel(const bf16* __restrict__ q, const bf16* __restri
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int kb = kb0 + (u * NW + wave) * STEP;
+      // A K load instruction covers 64 bytes of each of 16 rows, half of a
+      // 128-byte cache line, and the next one the other half: without the
+      // non-temporal hint the line stays in L2 between the two, so the
+      // cache is fetched once (with it, 3.6% of K was fetched twice and the
+      // kernel streamed 5% slower).  V rows are read whole, non-temporally.
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
         for (int t = 0; t < KT; ++t)
-          kr[u][bb][t] = buf_load16_nt(Kr, ((uint32_t)(kb + krow0 + 4 * bb) * D + 32 * t + 8 * g) * 2u);
+          kr[u][bb][t] = buf_load16(Kr, ((uint32_t)(kb + krow0 + 4 * bb) * D + 32 * t + 8 * g) * 2u);
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const uint32_t off = ((uint32_t)(kb + 8 * g + r) * D + NB * n) * 2u;
