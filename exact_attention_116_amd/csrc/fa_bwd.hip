@@ -347,20 +347,12 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds key my_key, features 32cb + 8(i/4) + 4g + i%4 ----
-  if (my_key < N) {
-    bf16* out = (role ? dk : dv) + ((size_t)bh * N + my_key) * D;
-    const float m = role ? scale : 1.f;
-#pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int d0 = 32 * cb + 8 * ii + 4 * g;
-        *reinterpret_cast<u32x2*>(out + d0) =
-            u32x2{pack16<F16>(m * acc[cb][4 * ii], m * acc[cb][4 * ii + 1]),
-                  pack16<F16>(m * acc[cb][4 * ii + 2], m * acc[cb][4 * ii + 3])};
-      }
-  }
+  // ---- epilogue: lane holds key my_key, features 32cb + 8(i/4) + 4g + i%4;
+  // whole rows of dV (role 0) or dK (role 1) through LDS, 32 rows per wave ----
+  static_assert(NW * 32 * RB <= (int)sizeof(smem), "output staging fits the tile buffers");
+  bf16* out = (role ? dk : dv) + (size_t)bh * N * D;
+  store_tile_rows<F16, D>(smem + wave * 32 * RB, acc, role ? scale : 1.f, lane, N - kw,
+                          [&](int r) { return out + (size_t)(kw + r) * D; });
 }
 
 // ---------------------------------------------------------------------------
@@ -504,18 +496,10 @@ void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     __syncthreads();
   }
 
-  if (my_q < N) {
-    const size_t row = (size_t)bh * N + my_q;
-#pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int d0 = 32 * cb + 8 * ii + 4 * g;
-        *reinterpret_cast<u32x2*>(dq + row * D + d0) =
-            u32x2{pack16<F16>(scale * acc[cb][4 * ii], scale * acc[cb][4 * ii + 1]),
-                  pack16<F16>(scale * acc[cb][4 * ii + 2], scale * acc[cb][4 * ii + 3])};
-      }
-  }
+  // whole dQ rows through LDS, 32 rows per wave
+  static_assert(NW * 32 * RB <= (int)sizeof(smem), "output staging fits the tile buffers");
+  store_tile_rows<F16, D>(smem + wave * 32 * RB, acc, scale, lane, N - qw,
+                          [&](int r) { return dq + ((size_t)bh * N + qw + r) * D; });
 }
 
 // ---------------------------------------------------------------------------

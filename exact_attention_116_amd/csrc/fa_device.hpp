@@ -171,4 +171,35 @@ __device__ __forceinline__ float dot2_16(uint32_t a, uint32_t b, float acc) {
   else return dot2_bf16(a, b, acc);
 }
 
+// Store a wave's 32 x D tile of 16-bit outputs held in the 32x32 MFMA
+// accumulator layout (lane l: row l%32; acc[cb][i] is feature
+// 32cb + 8(i/4) + 4(l/32) + i%4), each value times mul, as whole rows: the
+// tile is staged in LDS (32 * 2D bytes at lds, 16-byte chunks XOR-swizzled
+// by row so that both passes are free of bank conflicts) and read back so
+// that 2D/16 lanes store one row, instead of 8 bytes per row and lane.
+// row(r) is the destination of tile row r; rows r >= nrows are not written.
+// The caller guarantees that nothing else uses those LDS bytes meanwhile.
+template <bool F16, int D, typename RowPtr>
+__device__ __forceinline__ void store_tile_rows(uint8_t* lds, const f32x16 (&acc)[D / 32], float mul,
+                                                int lane, int nrows, RowPtr row) {
+  constexpr int RB = D * 2, NCH = RB / 16;
+  const int l32 = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int ch = 4 * cb + ii;
+      *reinterpret_cast<u32x2*>(lds + l32 * RB + 16 * (ch ^ (l32 % NCH)) + 8 * g) =
+          u32x2{pack16<F16>(acc[cb][4 * ii] * mul, acc[cb][4 * ii + 1] * mul),
+                pack16<F16>(acc[cb][4 * ii + 2] * mul, acc[cb][4 * ii + 3] * mul)};
+    }
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's rows are in LDS
+#pragma unroll
+  for (int k = 0; k < 32 * NCH / 64; ++k) {
+    const int L = 64 * k + lane, r = L / NCH, ch = L % NCH;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(lds + r * RB + 16 * (ch ^ (r % NCH)));
+    if (r < nrows) *reinterpret_cast<u32x4*>(row(r) + 8 * ch) = val;
+  }
+}
+
 }  // namespace fa

@@ -350,29 +350,11 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         }
     }
   } else {
-    // 16-bit output: each wave stages its 32 rows in LDS (free after the
-    // last tile's barrier), 16-byte chunks XOR-swizzled by row, and reads
-    // them back so that 16 lanes store one whole row: every store
-    // instruction writes 64 x 16 contiguous bytes per row group instead of
-    // 8 bytes in each of 32 rows.
-    uint8_t* Os = reinterpret_cast<uint8_t*>(smem) + wave * 32 * RB;
-#pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int c = 4 * cb + ii;
-        *reinterpret_cast<u32x2*>(Os + l32 * RB + 16 * (c ^ (l32 % NCH)) + 8 * g) =
-            u32x2{pack16<F16>(acc[cb][4 * ii] * inv, acc[cb][4 * ii + 1] * inv),
-                  pack16<F16>(acc[cb][4 * ii + 2] * inv, acc[cb][4 * ii + 3] * inv)};
-      }
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's rows are in LDS
-#pragma unroll
-    for (int k = 0; k < 32 * NCH / 64; ++k) {
-      const int L = 64 * k + lane, r = L / NCH, ch = L % NCH;
-      const u32x4 val = *reinterpret_cast<const u32x4*>(Os + r * RB + 16 * (ch ^ (r % NCH)));
-      if (qw + r < Lq)
-        *reinterpret_cast<u32x4*>(static_cast<bf16*>(o) + qbase + (size_t)(qw + r) * rs + 8 * ch) = val;
-    }
+    // 16-bit output: whole rows through LDS (free after the last tile's
+    // barrier), 8 KB per wave
+    bf16* ob = static_cast<bf16*>(o);
+    store_tile_rows<F16, D>(reinterpret_cast<uint8_t*>(smem) + wave * 32 * RB, acc, inv, lane, Lq - qw,
+                            [&](int r) { return ob + qbase + (size_t)(qw + r) * rs; });
   }
   if (my_q < Lq && g == 0) lse[lbase + my_q] = l > 0.f ? (m + __builtin_amdgcn_logf(l)) * kLn2 : kNegInf;
 }

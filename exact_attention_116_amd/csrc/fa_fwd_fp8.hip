@@ -368,31 +368,9 @@ void fa_fwd_fp8_dl_kernel(const uint8_t* __restrict__ q, const uint8_t* __restri
   l = sum_pair32(l);
   // acc holds 256 * sum_t (r_t / r_last) sum_j p_j code_j 2^(e_t - e_max)
   const float fac = __builtin_amdgcn_ldexpf(r_cur, e_max) / l;
-  // Each wave stages its 32 bf16 output rows in LDS (free after the last
-  // tile's barrier), 16-byte chunks XOR-swizzled by row, and stores them
-  // back as whole 256-byte rows, 16 lanes per row.
-  {
-    constexpr int ORB = D * 2;             // bytes per bf16 output row
-    constexpr int OCH = ORB / 16;          // 16-byte chunks per row
-    uint8_t* Os = smem + wave * 32 * ORB;
-#pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int ch = 4 * cb + ii;
-        *reinterpret_cast<u32x2*>(Os + l32 * ORB + 16 * (ch ^ (l32 % OCH)) + 8 * g) =
-            u32x2{pack_bf16(acc[cb][4 * ii] * fac, acc[cb][4 * ii + 1] * fac),
-                  pack_bf16(acc[cb][4 * ii + 2] * fac, acc[cb][4 * ii + 3] * fac)};
-      }
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's rows are in LDS
-#pragma unroll
-    for (int k = 0; k < 32 * OCH / 64; ++k) {
-      const int L = 64 * k + lane, r = L / OCH, ch = L % OCH;
-      const u32x4 val = *reinterpret_cast<const u32x4*>(Os + r * ORB + 16 * (ch ^ (r % OCH)));
-      if (qw + r < N)
-        *reinterpret_cast<u32x4*>(o + ((size_t)bh * N + qw + r) * D + 8 * ch) = val;
-    }
-  }
+  // whole output rows through LDS (free after the last tile's barrier)
+  store_tile_rows<false, D>(smem + wave * 32 * D * 2, acc, fac, lane, N - qw,
+                            [&](int r) { return o + ((size_t)bh * N + qw + r) * D; });
   if (my_q < N && g == 0)
     lse[(size_t)bh * N + my_q] = (m + __builtin_amdgcn_logf(l) - kLog2PScale) * kLn2;
 }
