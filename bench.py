@@ -44,31 +44,25 @@ PEAK_HBM_GBS = 8000.0
 
 # HBM bytes per launch, from rocprofv3 counter runs (FETCH_SIZE, then
 # WRITE_SIZE, KiB per dispatch, averaged over the dispatches of
-# `bench.py --only <w> --steps 2 --warmup 1 --copy-calibration`).  The same
-# counters read a 1 GiB device copy as 524300 KiB fetched and 1048576 KiB
-# written, so fetches are scaled by 1048576/524300 and writes by 1.  Each
+# `bench.py --only <w> --steps 2 --warmup 1 --copy-calibration`; kernels of
+# several launches per workload are summed).  The same counters read a 1 GiB
+# device copy as 524306 KiB fetched and 1048576 KiB written, so fetches are
+# scaled by 1048576/524306 and writes by 1.  Each
 # entry is tied to the SHA-256 of its kernel source plus the shared device
 # header: once either changes, the figure no longer describes the kernel and
 # the bench reports traffic as null.  (A digest is moved to a new source only
 # when the measured kernels' instructions were compared and found identical.)  Split-KV decode entries add the
 # split-merge kernel's counters to the split kernel's.
-COUNTER_SCALE = {"fetch": 1048576.0 / 524300.0, "write": 1.0}
+COUNTER_SCALE = {"fetch": 1048576.0 / 524306.0, "write": 1.0}
 TRAFFIC_KIB = {
-    "c3": {"src": ["fa_fwd_bf16.hip"], "fetch_kib": (262080.3125 + 283009.9375 + 281869.125) / 3,
-           "write_kib": 66560.0,
-           "sha256": "6d4e8e3753d4ebbb3c30cd503d69a7f789552180ce8b8d0050bc2dfbf6dfa972"},
-    "c4": {"src": ["fa_decode.hip"],
-           "fetch_kib": (4194784.0 + 4194625.0 + 4194618.0) / 3 + 4180.0,
-           "write_kib": (8706.0 + 8707.0 + 8705.0) / 3 + 72.0,
-           "sha256": "187fd05543296a83d140f0a11f7137c57d3ce55b56990ef77a7e9a2a10d0aa26"},
-    "c6": {"src": ["fa_decode_gqa.hip", "fa_decode.hip"],
-           "fetch_kib": (1085756.0 + 1086890.0 + 1087423.0) / 3 + (8342.0 + 8340.0 + 8340.0) / 3,
-           "write_kib": (17408.0 + 17411.0 + 17411.0) / 3 + 144.0,
-           "sha256": "cd7e9e57ac82ef64dc210b054d35238c404b389cf1db671cf7b6de1ec9215ba5"},
-    "c7": {"src": ["fa_decode_gqa.hip", "fa_decode.hip"],
-           "fetch_kib": (132958.0 + 132912.0 + 133009.0) / 3 + (4182.0 + 4180.0 + 4180.0) / 3,
-           "write_kib": 8704.0 + 72.0,
-           "sha256": "cd7e9e57ac82ef64dc210b054d35238c404b389cf1db671cf7b6de1ec9215ba5"},
+    "c3": {"src": ["fa_fwd_bf16.hip"], "fetch_kib": 244016.9, "write_kib": 66560.0,
+           "sha256": "c3f8f3fbd98a136499ed65e2627402bf336b4b19c93b838dc697b497d5b27ee7"},
+    "c4": {"src": ["fa_decode.hip"], "fetch_kib": 4198850.3, "write_kib": 8778.0,
+           "sha256": "1e3662cf3f97648d93cc1a4034999837128f01fc6c19c2efdc0f7e339d2ef68f"},
+    "c6": {"src": ["fa_decode_gqa.hip", "fa_decode.hip"], "fetch_kib": 1057821.5, "write_kib": 17681.8,
+           "sha256": "70464f796f4950ce16c88cb5b9c355c8cd93da0ed29b06a058bc176c7897950b"},
+    "c7": {"src": ["fa_decode_gqa.hip", "fa_decode.hip"], "fetch_kib": 135573.1, "write_kib": 8777.5,
+           "sha256": "70464f796f4950ce16c88cb5b9c355c8cd93da0ed29b06a058bc176c7897950b"},
 }
 
 
