@@ -24,7 +24,9 @@
 //     VGPRs as MFMA B operands.  Per 32-query block one wave forms
 //     S = Q K^T, P and dV^T += dO^T P, the other dP = dO V^T, then, with P
 //     handed over through LDS, dS and dK^T += Q^T dS (one key per lane
-//     column; P and dS go straight in as B operands).
+//     column; P and dS go straight in as B operands).  Each block's second
+//     product is deferred by one block, so that it overlaps the next
+//     block's exponentials and dS work.
 //  3. fa_bwd_dq_kernel: query tiles outer, key/value tiles inner, the
 //     forward kernel's layout: Q^T and dO^T stay in VGPRs, one query per lane
 //     column, S^T = K Q^T and dP^T = V dO^T, then dQ^T += K^T dS^T.
@@ -38,6 +40,8 @@
 // their 16-byte chunks are XOR-swizzled with a pattern that keeps both
 // reads free of bank conflicts: at 256 bytes per row, chunk c of row r sits
 // at c ^ (4*(r%4) + (r/4)%4).
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_internal.h"
 
@@ -71,13 +75,8 @@ struct TileLoader {
     }
   }
   __device__ __forceinline__ void load(rsrc_t R, uint32_t base_off, uint8_t* lds, int wave) const {
-#if defined(__HIP_DEVICE_COMPILE__)  // the LDS-DMA builtin exists in the device pass only
 #pragma unroll
-    for (int x = 0; x < IPW; ++x)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          R, (__attribute__((address_space(3))) void*)(lds + (wave * IPW + x) * 1024), 16,
-          base_off + goff[x], 0, 0, 0);
-#endif
+    for (int x = 0; x < IPW; ++x) lds_dma16(R, lds + (wave * IPW + x) * 1024, base_off + goff[x]);
   }
 };
 
@@ -166,12 +165,16 @@ __device__ __forceinline__ void lds_barrier() {
 // bf16 P its partner left in LDS, forms dS = P (dP - D) and
 // dK^T += Q^T dS.  With one resident operand and one accumulator per wave
 // (~190 registers; both on one wave would need ~350), eight waves -- two
-// per SIMD -- share a 128-key workgroup, and one wave's exponentials or dS
-// work run under the other's MFMAs.  Waves w and w + 4 form pair w (w < 4);
-// the lower-numbered (older) role-0 waves win the issue arbitration, which
-// is the order the hand-off needs.  Q and dO rows are read row-wise for the
-// first product and through ds_read_b64_tr_b16 for the second.
-template <int D, int BQ, bool CAUSAL, bool F16, int PD = 4>
+// per SIMD -- share a 128-key workgroup.  Waves w and w + 4 (one SIMD) form
+// pair w.  Per 32-query block the pair meets at one barrier (P handed over);
+// between two barriers role 0 forms S and P of block b while its dV^T update
+// for block b - 1 runs on the matrix cores, and role 1 forms dP of block b
+// while it computes dS of block b - 1, then adds block b - 1 into dK^T.
+// LSE and D enter as the starting values of the S and dP accumulators
+// (-LSE/scale and -D), so P = exp2(c s) and dS = P s without a per-element
+// correction.  Q and dO rows are read row-wise for the first product and
+// through ds_read_b64_tr_b16 for the second.
+template <int D, int BQ, bool CAUSAL, bool F16, int PD = 3>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512)))
 void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                              const bf16* __restrict__ v, const bf16* __restrict__ dout,
@@ -184,8 +187,12 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   constexpr int TILE = BQ * RB;         // bytes of one Q (or dO) tile
   constexpr int STAGE = 2 * TILE + 2 * BQ * 4;
   constexpr int PBLK = 32 * 32 * 2;     // one pair's bf16 P block
-  constexpr float kLog2e = 1.44269504088896340736f;
-  static_assert(BQ % 32 == 0 && 2 * ((BQ + 63) / 64) <= NW, "query tile of whole 32-row blocks");
+  constexpr int NB = BQ / 32;           // 32-query blocks per tile
+  constexpr int NC = D / 32, NF1 = D / 16, NF2 = 2 * NC;
+  // steps of the loops that interleave one product with the other role's
+  // eight pairs of exponentials (or dS values): at least eight
+  constexpr int NS1 = NF1 + PD > 8 ? NF1 + PD : 8, NS2 = NF2 + PD > 8 ? NF2 + PD : 8;
+  static_assert(BQ % 64 == 0 && NB % 2 == 0, "query tile of an even number of 32-row blocks");
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE + 2 * NP * PBLK];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -197,6 +204,7 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int k0 = kt * BC;
   const int kw = k0 + pair * 32;        // the pair's first key
   const int my_key = kw + l32;
+  const float neg_inv_scale = -1.f / scale;
 
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
@@ -205,7 +213,6 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   [[maybe_unused]] const rsrc_t Lr = make_rsrc(lse + (size_t)bh * N, (uint32_t)N * 4u);
   [[maybe_unused]] const rsrc_t Dr = make_rsrc(dsum + (size_t)bh * N, (uint32_t)N * 4u);
 
-  // K^T (role 0) or V^T (role 1) of this lane's key as B operands
   bf16x8 kv[D / 16];
   {
     const rsrc_t R = make_rsrc((role ? v : k) + head, head_bytes);
@@ -226,126 +233,188 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const uint32_t qoff = (uint32_t)it * BQ * RB;
     ld.load(Qr, qoff, st, wave);
     ld.load(Or, qoff, st + TILE, wave);
-#if defined(__HIP_DEVICE_COMPILE__)
-    if (wave < 2 * (BQ / 64 + (BQ % 64 != 0)) && lane < (BQ < 64 ? BQ : 64)) {
+    if (wave < 2 * (BQ / 64) && lane < 64) {
       const int which = wave & 1, part = wave >> 1;
       const uint32_t off = ((uint32_t)it * BQ + 64 * part + lane) * 4u;
-      uint8_t* dst = st + 2 * TILE + which * BQ * 4 + 64 * part * 4;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(which ? Dr : Lr,
-                                               (__attribute__((address_space(3))) void*)dst, 4,
-                                               off, 0, 0, 0);
+      lds_dma4(which ? Dr : Lr, st + 2 * TILE + which * BQ * 4 + 64 * part * 4, off);
     }
-#endif
   };
 
-  f32x16 acc[D / 32];                   // dV^T (role 0) or dK^T (role 1)
+  f32x16 acc[NC];                       // dV^T (role 0) or dK^T (role 1)
 #pragma unroll
-  for (int cb = 0; cb < D / 32; ++cb) acc[cb] = f32x16{};
+  for (int cb = 0; cb < NC; ++cb) acc[cb] = f32x16{};
 
-  if (it0 < nqt) {
-    load_tile(it0);
-    wait_vm();
-  }
+  if (it0 < nqt) load_tile(it0);
+  wait_vm();                            // also completes the K^T / V^T loads above
   __syncthreads();
 
-  for (int it = it0; it < nqt; ++it) {
-    const bool more = it + 1 < nqt;
-    if (more) load_tile(it + 1);
-    const uint8_t* st = smem + (it & 1) * STAGE;
-    const uint8_t* Qs = st;
-    const uint8_t* Os = st + TILE;
-    const float* Ls = reinterpret_cast<const float*>(st + 2 * TILE);
-    const float* Ds = Ls + BQ;
-    const uint8_t* A1 = role ? Os : Qs;   // row-wise operand of the first product
-    const uint8_t* A2 = role ? Qs : Os;   // transposed operand of the second
-    const float* X = role ? Ds : Ls;      // LSE (role 0) or D (role 1) per query
+  // The second product of each 32-query block (dV^T += dO^T P on role 0,
+  // dK^T += Q^T dS on role 1) is deferred to the next block's interval, where
+  // it runs beside that block's exponentials (role 0) or beside its
+  // dP MFMAs (role 1), instead of after a barrier with nothing to overlap.
+  // Every interval has the same shape: the workgroup's first interval defers
+  // products of zero P and dS, and blocks wholly before the pair's keys
+  // (causal) are computed and masked to zero like the diagonal blocks.  Each
+  // role runs its own copy of the loop (the same barriers in the same order),
+  // so each keeps only its own state live.
+  // P slots start at zero (the first interval's deferred dS reads one)
+  *reinterpret_cast<u32x4*>(smem + 2 * STAGE + tid * 16) = u32x4{0u, 0u, 0u, 0u};
+  *reinterpret_cast<u32x4*>(smem + 2 * STAGE + 8192 + tid * 16) = u32x4{0u, 0u, 0u, 0u};
+  static_assert(2 * NP * PBLK == 2 * 8192 && NW * 64 * 16 == 8192, "P slots cleared by one pass");
+  __syncthreads();
+
+  auto run = [&](auto ROLE) __attribute__((always_inline)) {
+    constexpr int R = decltype(ROLE)::value;
+    // the deferred block's transposed operand (the first tile's, for the
+    // first interval's zero products)
+    const uint8_t* pA2 = smem + (it0 & 1) * STAGE + (R ? 0 : TILE);
+    [[maybe_unused]] const uint8_t* ppb = smem + 2 * STAGE + (NP + pair) * PBLK;   // its P slot
+    int pr0 = 0;                        // its first row within the tile
+    [[maybe_unused]] bf16x8 pbo[2] = {};   // role 0: its P as B operands
+    [[maybe_unused]] f32x16 ps = f32x16{};   // role 1: its dP - D
+
+    auto second = [&](const bf16x8 (&bo)[2]) __attribute__((always_inline)) {
+      bf16x8 f[NF2];
+#pragma unroll
+      for (int i = 0; i < NF2 + PD; ++i) {
+        if (i < NF2) f[i] = rd.trfrag(pA2, pr0 + 16 * (i / NC), i % NC);
+        if (i >= PD) {
+          const int x = i - PD;
+          acc[x % NC] = mma16<F16>(f[x], bo[x / NC], acc[x % NC]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // role 1: dS of the deferred block, pair h, from its P (LDS) and dP - D
+    auto ds_pair = [&](const u32x4& lo, const u32x4& hi, int h) __attribute__((always_inline)) {
+      const int i = 2 * h;
+      const uint32_t w = h < 4 ? lo[h] : hi[h - 4];
+      return pack16<F16>(lo16<F16>(w) * ps[i], hi16<F16>(w) * ps[i + 1]);
+    };
+
+    for (int it = it0; it < nqt; ++it) {
+      const uint8_t* st = smem + (it & 1) * STAGE;
+      const uint8_t* Qs = st;
+      const uint8_t* Os = st + TILE;
+      const float* Ls = reinterpret_cast<const float*>(st + 2 * TILE);
+      const float* Ds = Ls + BQ;
 
 #pragma unroll
-    for (int blk = 0; blk < BQ / 32; ++blk) {
-      const int qb0 = it * BQ + 32 * blk;    // first query of the block
-      // false when every query of the block precedes every key of the pair
-      const bool act = !CAUSAL || qb0 + 31 >= kw;
-      // P slots alternate between blocks; a block that reuses the previous
-      // block's slot follows a tile barrier
-      uint8_t* pb = smem + 2 * STAGE + ((blk & 1) * NP + pair) * PBLK;
-      // accumulator row i is query qb0 + 8(i/4) + 4g + i%4; this lane's key
-      // is the column
-      f32x16 s = f32x16{};                  // S (role 0) or dP (role 1)
-      f32x4 x4[4];
-      uint32_t pw[8];
-      if (act) {
-#pragma unroll
-        for (int gi = 0; gi < 4; ++gi)
-          x4[gi] = *reinterpret_cast<const f32x4*>(X + 32 * blk + 8 * gi + 4 * g);
-        {
-          constexpr int NF = D / 16;
-          bf16x8 f[NF];
-#pragma unroll
-          for (int i = 0; i < NF + PD; ++i) {
-            if (i < NF) f[i] = rd.rowfrag(A1, 32 * blk, i);
-            if (i >= PD) s = mma16<F16>(f[i - PD], kv[i - PD], s);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-        if (role == 0) {
-          // P as bf16 pairs in B-operand order (slot j of k-step t is row 8t + j)
+      for (int blk = 0; blk < NB; ++blk) {
+        const int qb0 = it * BQ + 32 * blk;
+        uint8_t* pb = smem + 2 * STAGE + ((blk & 1) * NP + pair) * PBLK;
+        if constexpr (R == 0) {
           const bool edge = (CAUSAL && qb0 < kw + 31) || qb0 + 32 > N;
+          // ---- S - LSE/scale for this block (the accumulator starts at
+          // -LSE/scale, so exp2(c * s) is P) ----
+          f32x16 s;
 #pragma unroll
-          for (int h = 0; h < 8; ++h) {
-            const int i = 2 * h;
-            const float l0 = x4[i >> 2][i & 3] * kLog2e, l1 = x4[i >> 2][(i & 3) + 1] * kLog2e;
-            float p0 = __builtin_amdgcn_exp2f(fmaf(s[i], c, -l0));
-            float p1 = __builtin_amdgcn_exp2f(fmaf(s[i + 1], c, -l1));
-            if (edge) {
-              const int qi = qb0 + 8 * (i >> 2) + 4 * g + (i & 3);
-              if (qi >= N || (CAUSAL && my_key > qi)) p0 = 0.f;
-              if (qi + 1 >= N || (CAUSAL && my_key > qi + 1)) p1 = 0.f;
-            }
-            pw[h] = pack16<F16>(p0, p1);
+          for (int gi = 0; gi < 4; ++gi) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(Ls + 32 * blk + 8 * gi + 4 * g);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s[4 * gi + j] = x[j] * neg_inv_scale;
           }
+          {
+            bf16x8 f[NF1];
+#pragma unroll
+            for (int i = 0; i < NF1 + PD; ++i) {
+              if (i < NF1) f[i] = rd.rowfrag(Qs, 32 * blk, i);
+              if (i >= PD) s = mma16<F16>(f[i - PD], kv[i - PD], s);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+          // ---- P of this block, beside dV^T += dO^T P of the deferred block ----
+          uint32_t pw[8];
+          auto mix = [&](auto EDGE) __attribute__((always_inline)) {
+            constexpr bool ED = decltype(EDGE)::value;
+            bf16x8 f[NF2];
+#pragma unroll
+            for (int i = 0; i < NS2; ++i) {
+              if (i < NF2) f[i] = rd.trfrag(pA2, pr0 + 16 * (i / NC), i % NC);
+              if (i >= PD && i < NF2 + PD) {
+                const int x = i - PD;
+                acc[x % NC] = mma16<F16>(f[x], pbo[x / NC], acc[x % NC]);
+              }
+              if (i < 8) {
+                const int e = 2 * i;
+                float p0 = __builtin_amdgcn_exp2f(s[e] * c);
+                float p1 = __builtin_amdgcn_exp2f(s[e + 1] * c);
+                if constexpr (ED) {
+                  const int qi = qb0 + 8 * (e >> 2) + 4 * g + (e & 3);
+                  if (qi >= N || (CAUSAL && my_key > qi)) p0 = 0.f;
+                  if (qi + 1 >= N || (CAUSAL && my_key > qi + 1)) p1 = 0.f;
+                }
+                pw[i] = pack16<F16>(p0, p1);
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          };
+          if (edge) mix(std::true_type{});
+          else mix(std::false_type{});
           *reinterpret_cast<u32x4*>(pb + 16 * lane) = u32x4{pw[0], pw[1], pw[2], pw[3]};
           *reinterpret_cast<u32x4*>(pb + 1024 + 16 * lane) = u32x4{pw[4], pw[5], pw[6], pw[7]};
-        }
-      }
-      lds_barrier();                        // the block's P is in LDS
-      if (act) {
-        bf16x8 bo[2];                       // P (role 0) or dS (role 1) as B operands
-        if (role == 0) {
-          bo[0] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
-          bo[1] = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
+          pbo[0] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+          pbo[1] = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
+          pA2 = Os;
         } else {
-          // the partner's lane holds the same key and rows: read it lane for lane
-          const u32x4 lo = *reinterpret_cast<const u32x4*>(pb + 16 * lane);
-          const u32x4 hi = *reinterpret_cast<const u32x4*>(pb + 1024 + 16 * lane);
+          // ---- dP - D for this block (the accumulator starts at -D), beside
+          // dS of the deferred block ----
+          const u32x4 plo = *reinterpret_cast<const u32x4*>(ppb + 16 * lane);
+          const u32x4 phi = *reinterpret_cast<const u32x4*>(ppb + 1024 + 16 * lane);
+          f32x16 s;
+#pragma unroll
+          for (int gi = 0; gi < 4; ++gi) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(Ds + 32 * blk + 8 * gi + 4 * g);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s[4 * gi + j] = -x[j];
+          }
           uint32_t sw[8];
+          {
+            bf16x8 f[NF1];
 #pragma unroll
-          for (int h = 0; h < 8; ++h) {
-            const int i = 2 * h;
-            const uint32_t w = h < 4 ? lo[h] : hi[h - 4];
-            const float p0 = lo16<F16>(w), p1 = hi16<F16>(w);
-            sw[h] = pack16<F16>(p0 * (s[i] - x4[i >> 2][i & 3]),
-                              p1 * (s[i + 1] - x4[i >> 2][(i & 3) + 1]));
+            for (int i = 0; i < NS1; ++i) {
+              if (i < NF1) f[i] = rd.rowfrag(Os, 32 * blk, i);
+              if (i >= PD && i < NF1 + PD) s = mma16<F16>(f[i - PD], kv[i - PD], s);
+              if (i < 8) sw[i] = ds_pair(plo, phi, i);
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
-          bo[0] = __builtin_bit_cast(bf16x8, u32x4{sw[0], sw[1], sw[2], sw[3]});
-          bo[1] = __builtin_bit_cast(bf16x8, u32x4{sw[4], sw[5], sw[6], sw[7]});
+          // ---- dK^T += Q^T dS of the deferred block ----
+          const bf16x8 bo[2] = {__builtin_bit_cast(bf16x8, u32x4{sw[0], sw[1], sw[2], sw[3]}),
+                                __builtin_bit_cast(bf16x8, u32x4{sw[4], sw[5], sw[6], sw[7]})};
+          second(bo);
+          ps = s;
+          pA2 = Qs;
+          ppb = pb;
         }
-        constexpr int NC = D / 32, NF = 2 * NC;
-        bf16x8 f[NF];
-#pragma unroll
-        for (int i = 0; i < NF + PD; ++i) {
-          if (i < NF) f[i] = rd.trfrag(A2, 32 * blk + 16 * (i / NC), i % NC);
-          if (i >= PD) {
-            const int x = i - PD;
-            acc[x % NC] = mma16<F16>(f[x], bo[x / NC], acc[x % NC]);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        lds_barrier();                  // this block's P is in LDS
+        // the previous tile's stage is free once every wave is past the first
+        // block's interval (its last block was deferred into it)
+        if (blk == 0 && it + 1 < nqt) load_tile(it + 1);
+        pr0 = 32 * blk;
       }
+
+      if (it + 1 < nqt) wait_vm();
+      __syncthreads();
     }
 
-    if (more) wait_vm();
-    __syncthreads();
-  }
+    // ---- the last block's deferred second product ----
+    if constexpr (R == 0) {
+      second(pbo);
+    } else {
+      const u32x4 plo = *reinterpret_cast<const u32x4*>(ppb + 16 * lane);
+      const u32x4 phi = *reinterpret_cast<const u32x4*>(ppb + 1024 + 16 * lane);
+      uint32_t sw[8];
+#pragma unroll
+      for (int h = 0; h < 8; ++h) sw[h] = ds_pair(plo, phi, h);
+      const bf16x8 bo[2] = {__builtin_bit_cast(bf16x8, u32x4{sw[0], sw[1], sw[2], sw[3]}),
+                            __builtin_bit_cast(bf16x8, u32x4{sw[4], sw[5], sw[6], sw[7]})};
+      second(bo);
+    }
+  };
+  if (role == 0) run(std::integral_constant<int, 0>{});
+  else run(std::integral_constant<int, 1>{});
+  __syncthreads();                      // every wave is done with the tile buffers
 
   // ---- epilogue: lane holds key my_key, features 32cb + 8(i/4) + 4g + i%4;
   // whole rows of dV (role 0) or dK (role 1) through LDS, 32 rows per wave ----
@@ -372,7 +441,8 @@ void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   static_assert(BC % 32 == 0, "key tile of whole 32-key blocks");
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: the block skips are scalar branches
   const int l32 = lane & 31, g = lane >> 5;
   const int nqt = (N + BR - 1) / BR;
   const int bh = blockIdx.x % BH;

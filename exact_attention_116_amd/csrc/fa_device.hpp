@@ -132,6 +132,27 @@ __device__ __forceinline__ u32x2 buf_load8_nt(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 2));
 }
 
+// Direct global->LDS copies (buffer_load ... lds) of 16 or 4 bytes per lane
+// to lds + 16 * lane (or + 4 * lane).  Issued through inline asm rather than
+// the LDS-DMA builtin: after the builtin the compiler puts a vmcnt(0) wait in
+// front of the next transposing LDS read (ds_read_b64_tr_b16), whatever LDS
+// it reads, which makes a tile prefetch complete before the first transposed
+// product of the tile it is meant to overlap.  The copies write no registers;
+// the kernel itself waits for them (vmcnt(0), then a barrier) before any wave
+// reads the stage they fill.  M0 carries the LDS address.
+__device__ __forceinline__ void lds_dma16(rsrc_t r, const void* lds, uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t la = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds;
+  asm volatile("buffer_load_dwordx4 %1, %2, 0 offen lds" ::"{m0}"(la), "v"(off), "s"(r) : "memory");
+#endif
+}
+__device__ __forceinline__ void lds_dma4(rsrc_t r, const void* lds, uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t la = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds;
+  asm volatile("buffer_load_dword %1, %2, 0 offen lds" ::"{m0}"(la), "v"(off), "s"(r) : "memory");
+#endif
+}
+
 // Round two floats to bf16 (nearest even) and pack them (a in the low half).
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   bf16x2 p = {(bf16)a, (bf16)b};
