@@ -56,13 +56,13 @@ PEAK_HBM_GBS = 8000.0
 COUNTER_SCALE = {"fetch": 1048576.0 / 524306.0, "write": 1.0}
 TRAFFIC_KIB = {
     "c3": {"src": ["fa_fwd_bf16.hip"], "fetch_kib": 244016.9, "write_kib": 66560.0,
-           "sha256": "c3f8f3fbd98a136499ed65e2627402bf336b4b19c93b838dc697b497d5b27ee7"},
+           "sha256": "b00403d30dabc5859660cb34690c10169b7f26336333f7a3f5aaea25572cd97f"},
     "c4": {"src": ["fa_decode.hip"], "fetch_kib": 4198850.3, "write_kib": 8778.0,
-           "sha256": "1e3662cf3f97648d93cc1a4034999837128f01fc6c19c2efdc0f7e339d2ef68f"},
+           "sha256": "5e97611a26ac2cfece3c36bca4885bf4a61a66ef052765835b53367d362e873e"},
     "c6": {"src": ["fa_decode_gqa.hip", "fa_decode.hip"], "fetch_kib": 1057821.5, "write_kib": 17681.8,
-           "sha256": "70464f796f4950ce16c88cb5b9c355c8cd93da0ed29b06a058bc176c7897950b"},
+           "sha256": "5173b008bb12a55976be3113d7be1d4c27cdcd419827915ad4c16c6113ac15a9"},
     "c7": {"src": ["fa_decode_gqa.hip", "fa_decode.hip"], "fetch_kib": 135573.1, "write_kib": 8777.5,
-           "sha256": "70464f796f4950ce16c88cb5b9c355c8cd93da0ed29b06a058bc176c7897950b"},
+           "sha256": "5173b008bb12a55976be3113d7be1d4c27cdcd419827915ad4c16c6113ac15a9"},
 }
 
 
@@ -187,7 +187,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", default="all",
-                    help="all | c2c | c2n | c3 | c3h | c4 | c4s1 | c5 | q5 | c6 | c7 | c8 | b2c | b3 "
+                    help="all, or a comma list of: c2c c2n c3 c3h c4 c4s1 c5 q5 c6 c7 c8 b2c b3 "
                          "(profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy per step (for HBM counter scaling)")
@@ -212,7 +212,7 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
     jobs = []   # (name, launch-fn, flops, bytes, kind)
-    want = (lambda n: args.only in ("all", n))
+    want = (lambda n: args.only == "all" or n in args.only.split(","))
 
     w2, w3, w4, w5 = (fi.WORKLOADS[i] for i in (2, 3, 4, 5))
     if want("c2c") or want("c2n"):
