@@ -164,7 +164,8 @@ __device__ __forceinline__ void lds_barrier() {
 // P, and dV^T += dO^T P; role 1 holds V^T and forms dP = dO V^T, reads the
 // bf16 P its partner left in LDS, forms dS = P (dP - D) and
 // dK^T += Q^T dS.  With one resident operand and one accumulator per wave
-// (~190 registers; both on one wave would need ~350), eight waves -- two
+// (256 registers at d = 128 with the deferred products' state; both
+// operands and accumulators on one wave would need ~350), eight waves -- two
 // per SIMD -- share a 128-key workgroup.  Waves w and w + 4 (one SIMD) form
 // pair w.  Per 32-query block the pair meets at one barrier (P handed over);
 // between two barriers role 0 forms S and P of block b while its dV^T update
@@ -210,8 +211,8 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
   const rsrc_t Qr = make_rsrc(q + head, head_bytes);
   const rsrc_t Or = make_rsrc(dout + head, head_bytes);
-  [[maybe_unused]] const rsrc_t Lr = make_rsrc(lse + (size_t)bh * N, (uint32_t)N * 4u);
-  [[maybe_unused]] const rsrc_t Dr = make_rsrc(dsum + (size_t)bh * N, (uint32_t)N * 4u);
+  const rsrc_t Lr = make_rsrc(lse + (size_t)bh * N, (uint32_t)N * 4u);
+  const rsrc_t Dr = make_rsrc(dsum + (size_t)bh * N, (uint32_t)N * 4u);
 
   bf16x8 kv[D / 16];
   {
@@ -233,7 +234,7 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const uint32_t qoff = (uint32_t)it * BQ * RB;
     ld.load(Qr, qoff, st, wave);
     ld.load(Or, qoff, st + TILE, wave);
-    if (wave < 2 * (BQ / 64) && lane < 64) {
+    if (wave < 2 * (BQ / 64)) {           // LSE (even waves) and D (odd), 64 rows each
       const int which = wave & 1, part = wave >> 1;
       const uint32_t off = ((uint32_t)it * BQ + 64 * part + lane) * 4u;
       lds_dma4(which ? Dr : Lr, st + 2 * TILE + which * BQ * 4 + 64 * part * 4, off);
