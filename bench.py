@@ -24,8 +24,12 @@ One step = one pass of the whole hot path over resident synthetic inputs:
 ``value`` is the bf16 causal forward throughput over the N=2048 and N=16384
 workloads (their FLOPs over their summed kernel time, 4*B*H*N^2*d/2 per
 causal call); the decode bandwidth is reported beside it.  Each launch is
-bracketed by HIP events on the stream it runs on.  The CPU oracle is timed on
-a bounded sample of the same workloads (rank 0, N=1 only).
+bracketed by HIP events on the stream it runs on.  After the timed steps,
+C3, C2 causal, the ragged prefill and both backward workloads are also timed
+as 20 or more back-to-back launches under one event pair (``steady``): no
+event between launches, and no decode launch letting the clock recover.  The
+CPU oracle is timed on a bounded sample of the same workloads (rank 0, N=1
+only).
 """
 import argparse
 import json
@@ -413,27 +417,34 @@ def main():
     wall = time.perf_counter() - wall0
     ms_step = t_all0.elapsed_time(t_all1) / args.steps
 
-    # C3 back to back: K launches under one event pair, with no other
-    # workload between them (inside a step the memory-bound decode launches
-    # let the clock recover between the heavy ones)
-    steady = None
-    c3_job = next((j for j in jobs if j[0] == "c3"), None)
-    if c3_job is not None:
+    # Back to back: K launches of one workload under one event pair, with no
+    # other workload between them.  Inside a step the memory-bound decode
+    # launches let the clock recover between the heavy ones, and every launch
+    # there is bracketed by its own events, which leaves the GPU idle for some
+    # microseconds between kernels: for the short workloads a sizeable part of
+    # their in-step time.  C3's figure is the roofline's `steady`; the others
+    # sit beside their workloads.
+    steady_of = {}
+    for sname in ("c3", "c2c", "c8", "b2c", "b3"):
+        job = next((j for j in jobs if j[0] == sname), None)
+        if job is None:
+            continue
         n_steady = max(20, args.steps)
         for _ in range(3):
-            c3_job[1]()
+            job[1]()
         s0 = torch.cuda.Event(enable_timing=True)
         s1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         s0.record(stream)
         for _ in range(n_steady):
-            c3_job[1]()
+            job[1]()
         s1.record(stream)
         torch.cuda.synchronize()
         ms = s0.elapsed_time(s1) / n_steady
-        a = c3_job[2] / (ms * 1e-3) / 1e12
-        steady = {"launches": n_steady, "ms_mean": ms, "achieved": a, "peak": PEAK_BF16_TFLOPS,
-                  "unit": "TFLOP/s", "frac": a / PEAK_BF16_TFLOPS}
+        a = job[2] / (ms * 1e-3) / 1e12
+        steady_of[sname] = {"launches": n_steady, "ms_mean": ms, "achieved": a, "peak": PEAK_BF16_TFLOPS,
+                            "unit": "TFLOP/s", "frac": a / PEAK_BF16_TFLOPS}
+    steady = steady_of.get("c3")
 
     res = {}
     for i, (name, _, flops, nbytes, kind) in enumerate(jobs):
@@ -442,6 +453,8 @@ def main():
                      "ms_min": float(ts.min()), "flops": flops, "bytes": nbytes}
         if kind.startswith("fwd") or kind.startswith("bwd"):
             res[name]["tflops"] = flops / (ts.mean() * 1e-3) / 1e12
+            if name in steady_of:
+                res[name]["steady"] = steady_of[name]
         else:
             res[name]["gbs"] = nbytes / (ts.mean() * 1e-3) / 1e9
 
@@ -502,7 +515,8 @@ def main():
                   "roofline": {"kernel": "fa_fwd_bf16_kernel (packed)", "bound": "mfma",
                                "achieved": a, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                "frac": a / PEAK_BF16_TFLOPS, "traffic": None,
-                               "algorithmic_bytes": res["c8"]["bytes"]}}
+                               "algorithmic_bytes": res["c8"]["bytes"],
+                               "steady": steady_of.get("c8")}}
     fp16 = None
     if "c3h" in res:
         a = res["c3h"]["tflops"]
@@ -532,7 +546,8 @@ def main():
                                           "bound": "mfma", "achieved": a,
                                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                           "frac": a / PEAK_BF16_TFLOPS, "traffic": None,
-                                          "algorithmic_bytes": res[tag]["bytes"]}}
+                                          "algorithmic_bytes": res[tag]["bytes"],
+                                          "steady": steady_of.get(tag)}}
     prop = torch.cuda.get_device_properties(0)
     clock_khz = None
     try:   # hipDeviceAttributeClockRate (kHz), from the HIP runtime torch already loaded
