@@ -2,8 +2,8 @@
 //
 // Method (the "Flash Attention" Markdown note, sections "Tiling（分块）技术"
 // and "递归计算softmax"; loop order from the FlashAttention-2 overview):
-// queries are tiled in the outer loop (one workgroup per query tile of one
-// (batch, head)), keys/values in the inner loop.  For every key tile the
+// queries are tiled in the outer loop (a workgroup per two query tiles of
+// one (batch, head)), keys/values in the inner loop.  For every key tile the
 // kernel forms the scores, updates a running row max m and row sum l,
 // rescales the output accumulator by exp(m_old - m_new) and adds P*V.  The
 // N x N scores never leave registers.  The output is divided by l once at
@@ -56,10 +56,17 @@
 //    the cumulative lengths, and causal masking is aligned at the sequence
 //    end (query i sees key j iff j <= i + Lk - Lq).  A query that sees no
 //    key gets O = 0 and LSE = -inf.
-//    Query tiles are launched heaviest first.  Consecutive workgroups take
-//    different heads, so with B*H a multiple of 8 every query tile of a
-//    head lands on the same XCD (dispatch is round-robin over the 8 XCDs)
-//    and shares its K/V in that XCD's L2.
+//  * A workgroup computes two query tiles of one (sequence, head), one
+//    after the other: row r of the grid takes tiles nqt-1-r and r.  Under
+//    causal masking their key spans add up to the same length in every
+//    row, so the rows are balanced; the heavier tile runs first.  While the
+//    first tile's last key tile is computed, the second tile's first key
+//    tile is already loading into the other LDS stage, and its Q rows load
+//    during the first tile's epilogue, so only the first tile of each
+//    workgroup waits for its inputs.  Consecutive workgroups take different
+//    heads, so with B*H a multiple of 8 every query tile of a head lands on
+//    the same XCD (dispatch is round-robin over the 8 XCDs) and shares its
+//    K/V in that XCD's L2.
 #include "fa_device.hpp"
 #include "fa_internal.h"
 
@@ -122,28 +129,36 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     lbase = (size_t)bh * lay.N;
   }
   const int nqt = (Lq + C::BR - 1) / C::BR;
-  if constexpr (CAUSAL) qt = nqt - 1 - qt;  // longest query tiles first
-  if (qt < 0 || qt >= nqt) return;          // past this sequence's queries (whole workgroup)
+  // Row r of the grid takes query tiles nqt-1-r and r of this (sequence,
+  // head), in that order: under causal masking their KV spans add up to the
+  // same length in every row, and the second tile's first K/V tile and Q
+  // rows are fetched while the first one finishes.
+  const int row = qt;
+  if (row >= (nqt + 1) / 2) return;         // past this sequence's queries (whole workgroup)
+  const int nitems = nqt - 1 - row > row ? 2 : 1;
   const int off = CAUSAL ? Lk - Lq : 0;     // causal: query i sees keys j <= i + off
   const bf16* Qh = q + qbase;
   const bf16* Kh = k + kbase;
   const bf16* Vh = v + kbase;
   const uint32_t RG = (uint32_t)rs * 2u;    // bytes from one row to the next in HBM
 
-  const int q0 = qt * C::BR;
-  const int qw = q0 + wave * 32;   // first query of this wave
-  const int my_q = qw + l32;       // the query this lane's columns belong to
+  qt = nqt - 1 - row;
 
   const rsrc_t Qr = make_rsrc(Qh, (uint32_t)Lq * RG);
   [[maybe_unused]] const rsrc_t Kr = make_rsrc(Kh, (uint32_t)Lk * RG);
   [[maybe_unused]] const rsrc_t Vr = make_rsrc(Vh, (uint32_t)Lk * RG);
   bf16x8 qb[D / 16];
+  auto load_q = [&](int t) {
+    const int mq = t * C::BR + wave * 32 + l32;
 #pragma unroll
-  for (int u = 0; u < D / 16; ++u)
-    qb[u] = __builtin_bit_cast(bf16x8, buf_load16(Qr, (uint32_t)my_q * RG + (16u * u + 8u * g) * 2u));
-
-  const int kv_end = CAUSAL ? max(0, min(Lk, q0 + C::BR + off)) : Lk;
-  const int ntiles = (kv_end + BC - 1) / BC;
+    for (int u = 0; u < D / 16; ++u)
+      qb[u] = __builtin_bit_cast(bf16x8, buf_load16(Qr, (uint32_t)mq * RG + (16u * u + 8u * g) * 2u));
+  };
+  auto tiles_of = [&](int t) {
+    const int kv_end = CAUSAL ? max(0, min(Lk, t * C::BR + C::BR + off)) : Lk;
+    return (kv_end + BC - 1) / BC;
+  };
+  load_q(qt);
 
   // Direct global -> LDS loads.  One wave instruction fills 1 KB of LDS
   // (lane i -> bytes 16i..16i+15); the 16-byte chunk c of row r sits at
@@ -164,9 +179,10 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     gk[x] = (uint32_t)r * RG + (uint32_t)(16 * (p ^ (r % NCH)));
     gv[x] = (uint32_t)r * RG + (uint32_t)(16 * (p ^ (2 * (r & 3))));
   }
-  auto load_tile = [&](int j) {
+  // key tile j into LDS stage st
+  auto load_tile = [&](int j, int st) {
     [[maybe_unused]] const uint32_t tile = (uint32_t)j * BC * RG;
-    uint8_t* Kd = reinterpret_cast<uint8_t*>(smem + (j & 1) * (C::KTILE + C::VTILE));
+    uint8_t* Kd = reinterpret_cast<uint8_t*>(smem + (st & 1) * (C::KTILE + C::VTILE));
     [[maybe_unused]] uint8_t* Vd = Kd + C::KTILE * 2;
 #if defined(__HIP_DEVICE_COMPILE__)  // the LDS-DMA builtin exists in the device pass only
 #pragma unroll
@@ -196,174 +212,200 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       v_rd[cb] = (uint32_t)(r * RB + 16 * (c ^ (2 * (r & 3))) + 8 * (j16 & 1));
     }
   }
-  f32x16 acc[D / 32];
+  int gt = 0;                // tiles computed so far (LDS stage = gt & 1)
+  int ntiles = tiles_of(qt);
+  bool loaded = false;       // the current query tile's first key tile is in stage gt & 1
+
+  for (int item = 0; item < nitems; ++item) {
+    if (item == 1) qt = row;
+    if (!loaded) {
+      if (ntiles > 0) load_tile(0, gt);
+      wait_loads();            // also the Q rows
+      __syncthreads();
+    }
+    const int q0 = qt * C::BR;
+    const int qw = q0 + wave * 32;   // first query of this wave
+    const int my_q = qw + l32;       // the query this lane's columns belong to
+    const int ntiles_next = item + 1 < nitems ? tiles_of(row) : 0;
+    f32x16 acc[D / 32];
 #pragma unroll
-  for (int cb = 0; cb < D / 32; ++cb) acc[cb] = f32x16{};
-  float m = kNegInf;   // reference max, base-2 units of the scaled scores
-  float l = 0.f;       // this lane's share of the row sum (keys of its half)
+    for (int cb = 0; cb < D / 32; ++cb) acc[cb] = f32x16{};
+    float m = kNegInf;   // reference max, base-2 units of the scaled scores
+    float l = 0.f;       // this lane's share of the row sum (keys of its half)
 
-  load_tile(0);
-  wait_loads();
-  __syncthreads();
+    for (int j = 0; j < ntiles; ++j, ++gt) {
+      const int buf = gt & 1;
+      // the next tile of this query tile, or the first of the next one
+      const bool more = j + 1 < ntiles || ntiles_next > 0;
+      if (more) load_tile(j + 1 < ntiles ? j + 1 : 0, gt + 1);
+      loaded = more;
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    const bool more = j + 1 < ntiles;
-    if (more) load_tile(j + 1);
+      const int kb = j * BC;
+      const bool active = !CAUSAL || kb <= qw + 31 + off;
+      if (active) {
+        const bf16* Ks = smem + buf * (C::KTILE + C::VTILE);
+        const bf16* Vs = Ks + C::KTILE;
 
-    const int kb = j * BC;
-    const bool active = !CAUSAL || kb <= qw + 31 + off;
-    if (active) {
-      const bf16* Ks = smem + buf * (C::KTILE + C::VTILE);
-      const bf16* Vs = Ks + C::KTILE;
-
-      // ---- S^T = K * Q^T : keys on rows, this lane's query on the column ----
-      f32x16 s[BC / 32];
+        // ---- S^T = K * Q^T : keys on rows, this lane's query on the column ----
+        f32x16 s[BC / 32];
 #pragma unroll
-      for (int b = 0; b < BC / 32; ++b) s[b] = f32x16{};
-      {
-        // K fragments are read PD MFMAs ahead of their use; the scheduling
-        // fence after every step keeps the compiler from sinking each read
-        // next to its MFMA (which leaves only two LDS reads in flight)
-        constexpr int PDK = 4;
-        constexpr int NB = BC / 32, NQ = (D / 16) * NB;
-        bf16x8 kf[NQ];
+        for (int b = 0; b < BC / 32; ++b) s[b] = f32x16{};
+        {
+          // K fragments are read PD MFMAs ahead of their use; the scheduling
+          // fence after every step keeps the compiler from sinking each read
+          // next to its MFMA (which leaves only two LDS reads in flight)
+          constexpr int PDK = 4;
+          constexpr int NB = BC / 32, NQ = (D / 16) * NB;
+          bf16x8 kf[NQ];
 #pragma unroll
-        for (int i = 0; i < NQ + PDK; ++i) {
-          if (i < NQ) {
-            const int u = i / NB, b = i % NB;
-            kf[i] = *reinterpret_cast<const bf16x8*>(
-                reinterpret_cast<const uint8_t*>(Ks) + (32 * b) * RB + k_rd[u]);
+          for (int i = 0; i < NQ + PDK; ++i) {
+            if (i < NQ) {
+              const int u = i / NB, b = i % NB;
+              kf[i] = *reinterpret_cast<const bf16x8*>(
+                  reinterpret_cast<const uint8_t*>(Ks) + (32 * b) * RB + k_rd[u]);
+            }
+            if (i >= PDK) {
+              const int x = i - PDK, u = x / NB, b = x % NB;
+              s[b] = mma16<F16>(kf[x], qb[u], s[b]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
           }
-          if (i >= PDK) {
-            const int x = i - PDK, u = x / NB, b = x % NB;
-            s[b] = mma16<F16>(kf[x], qb[u], s[b]);
+        }
+
+        // ---- mask keys past the diagonal or past N (edge tiles only) ----
+        const bool edge = (CAUSAL && kb + BC - 1 > qw + off) || kb + BC > Lk;
+        if (edge) {
+#pragma unroll
+          for (int b = 0; b < BC / 32; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = kb + 32 * b + 8 * (i >> 2) + 4 * g + (i & 3);
+              const bool dead = key >= Lk || (CAUSAL && key > my_q + off);
+              s[b][i] = dead ? kNegInf : s[b][i];
+            }
+        }
+
+        // ---- online softmax (base 2) ----
+        // The tile is exponentiated against the reference max m without first
+        // taking its own max.  Its weights may then exceed 1 (exact in fp32
+        // and bf16); a tile whose weights sum to 2^8 or more on some lane
+        // (any weight above 2^8 among them, i.e. a max that grew by more than
+        // 8 in base 2), or a lane with no reference yet, takes the tile max,
+        // moves the reference there (O and l rescaled) and forms its weights
+        // again.  So the reference moves at least whenever the max-based lazy
+        // rule would move it, and the max over every score of a tile is taken
+        // only in those rare tiles.
+        const float l_in = l;
+        bf16x8 pb[BC / 16];
+        auto form_p = [&](float mref) __attribute__((always_inline)) {
+#pragma unroll
+          for (int t = 0; t < BC / 16; ++t) {
+            uint32_t w[4];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+              const float p0 = __builtin_amdgcn_exp2f(fmaf(s[t >> 1][8 * (t & 1) + 2 * h], c, -mref));
+              const float p1 = __builtin_amdgcn_exp2f(fmaf(s[t >> 1][8 * (t & 1) + 2 * h + 1], c, -mref));
+              w[h] = pack16<F16>(p0, p1);
+              l += p0 + p1;
+            }
+            pb[t] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
           }
-          __builtin_amdgcn_sched_barrier(0);
+        };
+        form_p(m == kNegInf ? 0.f : m);
+        if (__builtin_amdgcn_ballot_w64(!(l - l_in < 256.f) || m == kNegInf)) {
+          float mx = kNegInf;
+#pragma unroll
+          for (int b = 0; b < BC / 32; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[b][i]);
+          mx = max_pair32(mx) * c;
+          const float m_cand = fmaxf(m, mx);
+          const float alpha = (m_cand == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m - m_cand);
+          m = m_cand;
+#pragma unroll
+          for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[cb][i] *= alpha;
+          l = l_in * alpha;
+          form_p(m == kNegInf ? 0.f : m);
+        }
+
+        // ---- O^T += V^T * P^T ----
+        {
+          // V^T fragments, read PDV MFMAs ahead as for K
+          typedef short s16x4 __attribute__((ext_vector_type(4)));
+          constexpr int PDV = 4;
+          constexpr int NC = D / 32, NV = (BC / 16) * NC;
+          bf16x8 vf[NV];
+#pragma unroll
+          for (int i = 0; i < NV + PDV; ++i) {
+            if (i < NV) {
+              const int t = i / NC, cb = i % NC;
+              const uint8_t* vp = reinterpret_cast<const uint8_t*>(Vs) + (16 * t) * RB + v_rd[cb];
+              const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) s16x4*)(vp));
+              const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) s16x4*)(vp + 8 * RB));
+              vf[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+            if (i >= PDV) {
+              const int x = i - PDV, t = x / NC, cb = x % NC;
+              acc[cb] = mma16<F16>(vf[x], pb[t], acc[cb]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
 
-      // ---- mask keys past the diagonal or past N (edge tiles only) ----
-      const bool edge = (CAUSAL && kb + BC - 1 > qw + off) || kb + BC > Lk;
-      if (edge) {
-#pragma unroll
-        for (int b = 0; b < BC / 32; ++b)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kb + 32 * b + 8 * (i >> 2) + 4 * g + (i & 3);
-            const bool dead = key >= Lk || (CAUSAL && key > my_q + off);
-            s[b][i] = dead ? kNegInf : s[b][i];
-          }
-      }
+      if (more) wait_loads();
+      __syncthreads();
+    }
 
-      // ---- online softmax (base 2) ----
-      // The tile is exponentiated against the reference max m without first
-      // taking its own max.  Its weights may then exceed 1 (exact in fp32
-      // and bf16); a tile whose weights sum to 2^8 or more on some lane
-      // (any weight above 2^8 among them, i.e. a max that grew by more than
-      // 8 in base 2), or a lane with no reference yet, takes the tile max,
-      // moves the reference there (O and l rescaled) and forms its weights
-      // again.  So the reference moves at least whenever the max-based lazy
-      // rule would move it, and the max over every score of a tile is taken
-      // only in those rare tiles.
-      const float l_in = l;
-      bf16x8 pb[BC / 16];
-      auto form_p = [&](float mref) __attribute__((always_inline)) {
-#pragma unroll
-        for (int t = 0; t < BC / 16; ++t) {
-          uint32_t w[4];
-#pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[t >> 1][8 * (t & 1) + 2 * h], c, -mref));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[t >> 1][8 * (t & 1) + 2 * h + 1], c, -mref));
-            w[h] = pack16<F16>(p0, p1);
-            l += p0 + p1;
-          }
-          pb[t] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
-        }
-      };
-      form_p(m == kNegInf ? 0.f : m);
-      if (__builtin_amdgcn_ballot_w64(!(l - l_in < 256.f) || m == kNegInf)) {
-        float mx = kNegInf;
-#pragma unroll
-        for (int b = 0; b < BC / 32; ++b)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[b][i]);
-        mx = max_pair32(mx) * c;
-        const float m_cand = fmaxf(m, mx);
-        const float alpha = (m_cand == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m - m_cand);
-        m = m_cand;
+    // the epilogue's per-lane addresses are computed here, not kept live
+    // across the loops (the compiler would hoist them out of the item loop)
+    int lane_e = lane;
+    asm volatile("" : "+v"(lane_e));
+    // the next query tile's Q rows, while this one is stored
+    if (item + 1 < nitems) load_q(row);
+
+    // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2 (0 and -inf for a
+    // query that saw no key) ----
+    l = sum_pair32(l);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    if constexpr (OUT_F32) {
+      if (my_q < Lq) {
+        const size_t orow = qbase + (size_t)my_q * rs;
 #pragma unroll
         for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) acc[cb][i] *= alpha;
-        l = l_in * alpha;
-        form_p(m == kNegInf ? 0.f : m);
-      }
-
-      // ---- O^T += V^T * P^T ----
-      {
-        // V^T fragments, read PDV MFMAs ahead as for K
-        typedef short s16x4 __attribute__((ext_vector_type(4)));
-        constexpr int PDV = 4;
-        constexpr int NC = D / 32, NV = (BC / 16) * NC;
-        bf16x8 vf[NV];
-#pragma unroll
-        for (int i = 0; i < NV + PDV; ++i) {
-          if (i < NV) {
-            const int t = i / NC, cb = i % NC;
-            const uint8_t* vp = reinterpret_cast<const uint8_t*>(Vs) + (16 * t) * RB + v_rd[cb];
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(vp));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(vp + 8 * RB));
-            vf[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          for (int ii = 0; ii < 4; ++ii) {
+            const int d0 = 32 * cb + 8 * ii + 4 * g;
+            *reinterpret_cast<f32x4*>(static_cast<float*>(o) + orow + d0) =
+                f32x4{acc[cb][4 * ii] * inv, acc[cb][4 * ii + 1] * inv, acc[cb][4 * ii + 2] * inv,
+                      acc[cb][4 * ii + 3] * inv};
           }
-          if (i >= PDV) {
-            const int x = i - PDV, t = x / NC, cb = x % NC;
-            acc[cb] = mma16<F16>(vf[x], pb[t], acc[cb]);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
       }
+    } else {
+      // 16-bit output: whole rows through LDS (free after the last tile's
+      // barrier), 8 KB per wave
+      bf16* ob = static_cast<bf16*>(o);
+      // staged in the LDS stage of the last tile, not the one holding the
+      // next query tile's first key tile
+      store_tile_rows<F16, D>(reinterpret_cast<uint8_t*>(smem + ((gt + 1) & 1) * (C::KTILE + C::VTILE)) + wave * 32 * RB,
+                              acc, inv, lane_e, Lq - qw,
+                              [&](int r) { return ob + qbase + (size_t)(qw + r) * rs; });
     }
-
-    if (more) wait_loads();
-    __syncthreads();
+    if (my_q < Lq && g == 0) lse[lbase + my_q] = l > 0.f ? (m + __builtin_amdgcn_logf(l)) * kLn2 : kNegInf;
+    ntiles = ntiles_next;
+    if (item + 1 < nitems) __syncthreads();   // staging read back before the next tile loads land
   }
-
-  // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2 (0 and -inf for a
-  // query that saw no key) ----
-  l = sum_pair32(l);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  if constexpr (OUT_F32) {
-    if (my_q < Lq) {
-      const size_t orow = qbase + (size_t)my_q * rs;
-#pragma unroll
-      for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int d0 = 32 * cb + 8 * ii + 4 * g;
-          *reinterpret_cast<f32x4*>(static_cast<float*>(o) + orow + d0) =
-              f32x4{acc[cb][4 * ii] * inv, acc[cb][4 * ii + 1] * inv, acc[cb][4 * ii + 2] * inv,
-                    acc[cb][4 * ii + 3] * inv};
-        }
-    }
-  } else {
-    // 16-bit output: whole rows through LDS (free after the last tile's
-    // barrier), 8 KB per wave
-    bf16* ob = static_cast<bf16*>(o);
-    store_tile_rows<F16, D>(reinterpret_cast<uint8_t*>(smem) + wave * 32 * RB, acc, inv, lane, Lq - qw,
-                            [&](int r) { return ob + qbase + (size_t)(qw + r) * rs; });
-  }
-  if (my_q < Lq && g == 0) lse[lbase + my_q] = l > 0.f ? (m + __builtin_amdgcn_logf(l)) * kLn2 : kNegInf;
 }
 
 template <int D, int BC, int NW, bool CAUSAL, bool OUT_F32, bool F16>
 static hipError_t launch(const FwdArgs& a) {
   using C = FwdCfg<D, BC, NW>;
   const int nqt = (a.N + C::BR - 1) / C::BR;   // of the longest sequence
-  const long long blocks = (long long)nqt * a.B * a.H;
+  const long long blocks = (long long)((nqt + 1) / 2) * a.B * a.H;   // two query tiles per workgroup
   const FwdLayout lay{a.cu_q, a.cu_k, a.H, a.N, a.Nk, a.total_q, a.total_k};
   hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, BC, NW, CAUSAL, OUT_F32, F16>), dim3((unsigned)blocks),
                      dim3(C::NT), 0, (hipStream_t)a.stream, (const bf16*)a.q, (const bf16*)a.k,
