@@ -59,8 +59,8 @@ PEAK_HBM_GBS = 8000.0
 # split-merge kernel's counters to the split kernel's.
 COUNTER_SCALE = {"fetch": 1048576.0 / 524306.0, "write": 1.0}
 TRAFFIC_KIB = {
-    "c3": {"src": ["fa_fwd_bf16.hip"], "fetch_kib": 244016.9, "write_kib": 66560.0,
-           "sha256": "b00403d30dabc5859660cb34690c10169b7f26336333f7a3f5aaea25572cd97f"},
+    "c3": {"src": ["fa_fwd_bf16.hip"], "fetch_kib": 211522.9, "write_kib": 68608.0,
+           "sha256": "12aac91df1f600d802e5741b2944d89b73768addfba3dd87ea15de24c66e5242"},
     "c4": {"src": ["fa_decode.hip"], "fetch_kib": 4198850.3, "write_kib": 8778.0,
            "sha256": "5e97611a26ac2cfece3c36bca4885bf4a61a66ef052765835b53367d362e873e"},
     "c6": {"src": ["fa_decode_gqa.hip", "fa_decode.hip"], "fetch_kib": 1057821.5, "write_kib": 17681.8,
