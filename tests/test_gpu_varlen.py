@@ -47,6 +47,10 @@ CASES = [
     ([7, 100, 256, 33], [50, 612, 256, 1000]),                 # prefill chunks against cached keys
     ([40, 300, 5], [9, 200, 1]),                               # more queries than keys
     ([1, 1, 1, 1], [1000, 3, 64, 257]),                        # one query per sequence
+    # several 256-query tiles per sequence, paired in one workgroup (tiles 2 and
+    # 0, then 1): in the first sequence the first query tile sees no key at all
+    # while its partner sees one key tile
+    ([600, 513, 40], [40, 700, 300]),
 ]
 
 
