@@ -19,7 +19,8 @@ attention   the plain definition O = softmax(scale*Q*K^T)*V with its
             sequence end); the gradients dQ, dK, dV of the
             definition (the chain rule through the row softmax, P recomputed
             from Q and K), also for selected query rows (dQ) or selected
-            key rows (dK, dV) only; the elementwise error bound of
+            key rows (dK, dV) only, and over packed sequences of unequal
+            lengths; the elementwise error bound of
             an fp8-P kernel; attention with only P rounded to E4M3FN (the
             yardstick for an fp8 kernel's mean error).
 rotation    incoherent processing for fp8: the random-sign Walsh-Hadamard
@@ -34,7 +35,8 @@ from .codecs import decode_bf16, decode_e4m3fn, decode_f16, dequant_fp8_rows, ro
 from .attention import (  # noqa: F401
     attention, attention_rows, split_bounds, split_partials, merge_partials,
     decode_attention, decode_attention_gqa, fp8_p_error_bound, fp8_p_attention,
-    attention_backward, attention_backward_rows, attention_backward_keys, attention_varlen,
+    attention_backward, attention_backward_rows, attention_backward_keys, attention_backward_varlen,
+    attention_varlen,
     decode_attention_ragged,
 )
 from .rotation import hadamard_matrix, incoherent_rotation, quantize_e4m3_blocks  # noqa: F401

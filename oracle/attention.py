@@ -187,6 +187,54 @@ def attention_backward(q, k, v, do, scale, causal=False, row_block=ROW_BLOCK):
             dV.reshape(lead + vf.shape[-2:]))
 
 
+def attention_backward_varlen(q, k, v, do, cu_q, cu_k, scale, causal=False):
+    """Gradients of sum(O * dO) for ``attention_varlen``: packed sequences of
+    unequal lengths, causal masking aligned at the end of each sequence
+    (query i sees key j iff j <= i + (Lk - Lq)).
+
+    The same chain rule as ``_backward_rows`` per (sequence, head):
+        dV = P^T dO,  dP = dO V^T,  dS = P * (dP - sum_j P * dP),
+        dQ = scale * dS K,  dK = scale * dS^T Q,
+    where a query that sees no key has P = 0 (its output is the constant 0),
+    so it gets dQ = 0 and adds nothing to dK and dV; keys of a sequence with
+    no queries get dK = dV = 0.
+
+    q, do: [total_q, H, d]; k, v: [total_k, H, d]; cu_q, cu_k: the B+1
+    offsets.  Returns (dQ [total_q, H, d], dK [total_k, H, d],
+    dV [total_k, H, d]).
+    """
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    H = q.shape[1]
+    dQ = np.zeros_like(q)
+    dK = np.zeros_like(k)
+    dV = np.zeros_like(v)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        Lq, Lk = q1 - q0, k1 - k0
+        if Lq == 0 or Lk == 0:
+            continue
+        for h in range(H):
+            qs, ks, vs, dos = q[q0:q1, h], k[k0:k1, h], v[k0:k1, h], do[q0:q1, h]
+            S = scale * (qs @ ks.T)                                  # [Lq, Lk]
+            if causal:
+                i = np.arange(Lq)[:, None]
+                j = np.arange(Lk)[None, :]
+                S = np.where(j <= i + (Lk - Lq), S, -np.inf)
+            m = S.max(axis=1)
+            seen = np.isfinite(m)
+            ms = np.where(seen, m, 0.0)
+            E = np.exp(S - ms[:, None])
+            l = E.sum(axis=1)
+            with np.errstate(invalid="ignore", divide="ignore"):
+                P = np.where(seen[:, None], E / l[:, None], 0.0)
+            dP = dos @ vs.T
+            dS = P * (dP - (P * dP).sum(axis=1)[:, None])
+            dQ[q0:q1, h] = scale * (dS @ ks)
+            dK[k0:k1, h] = scale * (dS.T @ qs)
+            dV[k0:k1, h] = P.T @ dos
+    return dQ, dK, dV
+
+
 def attention_backward_rows(q_rows, qidx, k, v, do_rows, scale, causal=False):
     """dQ for selected query rows of one (batch, head): the query-side
     gradient of a row needs only that row's scores, probabilities and dO.

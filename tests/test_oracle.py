@@ -656,6 +656,126 @@ def test_varlen_against_torch_masked_sdpa():
 
 
 # ---------------------------------------------------------------------------
+# backward over ragged batches
+# ---------------------------------------------------------------------------
+
+def _varlen_loss(q, k, v, do, cuq, cuk, scale, causal):
+    O, _ = oracle.attention_varlen(q, k, v, cuq, cuk, scale, causal)
+    return float(np.sum(O * do))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_varlen_finite_differences(causal):
+    """Central differences of sum(O * dO) through the packed forward
+    definition, with more queries than keys in one sequence (its first
+    queries see no key under causal masking), more keys than queries in
+    another, and an empty query range."""
+    rng = np.random.default_rng(91 + causal)
+    H, d, scale, h = 2, 3, 0.7, 1e-5
+    lq, lk = [3, 2, 0, 4], [2, 5, 3, 4]
+    q, cuq = _pack(rng, lq, H, d)
+    k, cuk = _pack(rng, lk, H, d)
+    v, _ = _pack(rng, lk, H, d)
+    do, _ = _pack(rng, lq, H, d)
+    dQ, dK, dV = oracle.attention_backward_varlen(q, k, v, do, cuq, cuk, scale, causal)
+    for x, g in ((q, dQ), (k, dK), (v, dV)):
+        num = np.empty_like(x)
+        for idx in np.ndindex(*x.shape):
+            x0 = x[idx]
+            x[idx] = x0 + h
+            lp = _varlen_loss(q, k, v, do, cuq, cuk, scale, causal)
+            x[idx] = x0 - h
+            lm = _varlen_loss(q, k, v, do, cuq, cuk, scale, causal)
+            x[idx] = x0
+            num[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=0, atol=1e-8)
+    # the empty query range leaves its keys without gradient
+    assert np.all(dK[cuk[2]:cuk[3]] == 0.0) and np.all(dV[cuk[2]:cuk[3]] == 0.0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_varlen_against_torch_autograd(causal):
+    """torch float64 autograd through an explicitly masked softmax, per
+    sequence; rows with no visible key produce the constant 0."""
+    rng = np.random.default_rng(93 + causal)
+    H, d, scale = 3, 8, 0.45
+    lq, lk = [9, 3, 12, 1], [4, 10, 12, 30]
+    q, cuq = _pack(rng, lq, H, d)
+    k, cuk = _pack(rng, lk, H, d)
+    v, _ = _pack(rng, lk, H, d)
+    do, _ = _pack(rng, lq, H, d)
+    dQ, dK, dV = oracle.attention_backward_varlen(q, k, v, do, cuq, cuk, scale, causal)
+    for b in range(len(lq)):
+        Lq, Lk = lq[b], lk[b]
+        tq = torch.from_numpy(q[cuq[b]:cuq[b + 1]].transpose(1, 0, 2).copy()).requires_grad_()
+        tk = torch.from_numpy(k[cuk[b]:cuk[b + 1]].transpose(1, 0, 2).copy()).requires_grad_()
+        tv = torch.from_numpy(v[cuk[b]:cuk[b + 1]].transpose(1, 0, 2).copy()).requires_grad_()
+        if causal:
+            mask = torch.from_numpy(np.arange(Lk)[None, :] <= np.arange(Lq)[:, None] + (Lk - Lq))
+        else:
+            mask = torch.ones(Lq, Lk, dtype=torch.bool)
+        seen = mask.any(dim=1)
+        s = scale * (tq @ tk.transpose(1, 2))
+        s = s.masked_fill(~mask, float("-inf")).masked_fill(~seen[:, None], 0.0)
+        out = (torch.softmax(s, dim=-1) @ tv) * seen[:, None].to(torch.float64)
+        out.backward(torch.from_numpy(do[cuq[b]:cuq[b + 1]].transpose(1, 0, 2).copy()))
+        np.testing.assert_allclose(dQ[cuq[b]:cuq[b + 1]], tq.grad.numpy().transpose(1, 0, 2), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dK[cuk[b]:cuk[b + 1]], tk.grad.numpy().transpose(1, 0, 2), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dV[cuk[b]:cuk[b + 1]], tv.grad.numpy().transpose(1, 0, 2), rtol=0, atol=1e-12)
+        if causal and Lq > Lk:
+            assert np.all(dQ[cuq[b]:cuq[b] + Lq - Lk] == 0.0)
+
+
+def test_backward_varlen_chunk_is_tail_of_full_causal_backward():
+    """Lq new queries against Lk keys, end-aligned: the gradients equal those
+    of causal attention over the whole length-Lk sequence with an upstream
+    gradient that is zero on its first Lk - Lq rows."""
+    rng = np.random.default_rng(95)
+    H, d, scale = 2, 16, 0.3
+    for Lk, Lq in [(50, 7), (64, 64), (33, 1)]:
+        qf, kf, vf, dof = (_rand(rng, H, Lk, d) for _ in range(4))
+        dof[:, :Lk - Lq] = 0.0
+        dQf, dKf, dVf = oracle.attention_backward(qf, kf, vf, dof, scale, True)
+        t = (1, 0, 2)
+        dQ, dK, dV = oracle.attention_backward_varlen(
+            qf[:, Lk - Lq:].transpose(t), kf.transpose(t), vf.transpose(t),
+            dof[:, Lk - Lq:].transpose(t), [0, Lq], [0, Lk], scale, True)
+        np.testing.assert_allclose(dQ, dQf[:, Lk - Lq:].transpose(t), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dK, dKf.transpose(t), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dV, dVf.transpose(t), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_varlen_invariants(causal):
+    """Per (sequence, head): the key gradients sum to zero (each row of dS
+    sums to zero), dV sums to the sum of dO over the rows that see a key,
+    and no sequence's gradients depend on another sequence's data."""
+    rng = np.random.default_rng(97 + causal)
+    H, d, scale = 2, 8, 0.5
+    lq, lk = [20, 6, 13], [7, 40, 13]
+    q, cuq = _pack(rng, lq, H, d)
+    k, cuk = _pack(rng, lk, H, d)
+    v, _ = _pack(rng, lk, H, d)
+    do, _ = _pack(rng, lq, H, d)
+    dQ, dK, dV = oracle.attention_backward_varlen(q, k, v, do, cuq, cuk, scale, causal)
+    for b in range(3):
+        Lq, Lk = lq[b], lk[b]
+        sk = slice(cuk[b], cuk[b + 1])
+        np.testing.assert_allclose(dK[sk].sum(axis=0), 0.0, atol=1e-12)
+        first_seen = max(0, Lq - Lk) if causal else 0
+        np.testing.assert_allclose(dV[sk].sum(axis=0),
+                                   do[cuq[b] + first_seen:cuq[b + 1]].sum(axis=0), rtol=0, atol=1e-12)
+    # change sequence 1's data: sequences 0 and 2 keep their gradients
+    q2, k2, v2, do2 = (x.copy() for x in (q, k, v, do))
+    for x, cu in ((q2, cuq), (k2, cuk), (v2, cuk), (do2, cuq)):
+        x[cu[1]:cu[2]] = _rand(rng, cu[2] - cu[1], H, d)
+    g2 = oracle.attention_backward_varlen(q2, k2, v2, do2, cuq, cuk, scale, causal)
+    for b in (0, 2):
+        for g, gg, cu in zip((dQ, dK, dV), g2, (cuq, cuk, cuk)):
+            np.testing.assert_array_equal(g[cu[b]:cu[b + 1]], gg[cu[b]:cu[b + 1]])
+
+
+# ---------------------------------------------------------------------------
 # incoherent processing (random-sign Hadamard rotation) and block quantisation
 # ---------------------------------------------------------------------------
 
