@@ -20,7 +20,7 @@ EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_decode_splitkv", "fa_decode_workspace_byte
            "fa_decode_splitkv_ex", "fa_decode_splitkv_noalloc", "fa_decode_splitkv_gqa",
            "fa_decode_splitkv_varlen",
            "fa_fwd_varlen", "fa_fp8_quantize",
-           "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_ex",
+           "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_ex", "fa_bwd_varlen",
            "fa_status_string", "fa_last_error")
 
 
@@ -79,6 +79,8 @@ def load(path: str | None = None):
     lib.fa_bwd.restype = I
     lib.fa_bwd_ex.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, I, P, Z, P]
     lib.fa_bwd_ex.restype = I
+    lib.fa_bwd_varlen.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, Z, P]
+    lib.fa_bwd_varlen.restype = I
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
@@ -257,6 +259,24 @@ def fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtyp
                             _ptr(workspace, int(workspace_bytes), "workspace"),
                             int(workspace_bytes), _stream(stream)),
            "fa_bwd_ex")
+
+
+def fa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, B, H,
+                  max_seqlen_q, max_seqlen_k, total_q, total_k, d, scale, causal, workspace=None,
+                  workspace_bytes=0, stream=None):
+    """Packed bf16 q, o, dout, dq [total_q,H,d], k, v, dk, dv [total_k,H,d] and fp32
+    lse [H,total_q] (fa_fwd_varlen's outputs) -> bf16 dq, dk, dv."""
+    tq, tk, cu = 2 * _n(total_q, H, d), 2 * _n(total_k, H, d), 4 * _n(int(B) + 1)
+    _check(load().fa_bwd_varlen(_ptr(q, tq, "q", BF16), _ptr(k, tk, "k", BF16),
+                                _ptr(v, tk, "v", BF16), _ptr(o, tq, "o", BF16),
+                                _ptr(dout, tq, "dout", BF16), _ptr(lse, 4 * _n(H, total_q), "lse", F32),
+                                _ptr(dq, tq, "dq", BF16), _ptr(dk, tk, "dk", BF16),
+                                _ptr(dv, tk, "dv", BF16),
+                                _ptr(cu_seqlens_q, cu, "cu_seqlens_q", I32),
+                                _ptr(cu_seqlens_k, cu, "cu_seqlens_k", I32), B, H, max_seqlen_q,
+                                max_seqlen_k, total_q, total_k, d, float(scale), int(bool(causal)),
+                                _ptr(workspace, int(workspace_bytes), "workspace"),
+                                int(workspace_bytes), _stream(stream)), "fa_bwd_varlen")
 
 
 def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, max_seqlen_q, max_seqlen_k,

@@ -428,6 +428,67 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                    workspace_bytes, stream);
 }
 
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H,
+                        int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int d,
+                        float scale, int causal, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(FA_ERR_INVALID_ARG,
+                "q, k, v, o, dout, lse, dq, dk and dv must be non-NULL and 16-byte aligned");
+  if (!cu_seqlens_q || !cu_seqlens_k ||
+      ((reinterpret_cast<uintptr_t>(cu_seqlens_q) | reinterpret_cast<uintptr_t>(cu_seqlens_k)) & 3u))
+    return fail(FA_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_k must be non-NULL and 4-byte aligned");
+  if (B < 1 || H < 1) return fail(FA_ERR_INVALID_ARG, "B and H must be >= 1");
+  if (max_seqlen_q < 1 || max_seqlen_k < 1 || total_q < 1 || total_k < 1)
+    return fail(FA_ERR_INVALID_ARG, "max_seqlen_q, max_seqlen_k, total_q and total_k must be >= 1");
+  if (d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1");
+  if (!good_scale(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "varlen backward supports d = 64 or 128");
+  const int longest = max_seqlen_q > max_seqlen_k ? max_seqlen_q : max_seqlen_k;
+  if ((long long)B * H * ((longest + 31) / 32) > 0x7FFFFFFFLL ||
+      (long long)total_q * H > 0x7FFFFFFFLL)
+    return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
+  // one sequence of one head is addressed with 32-bit byte offsets over its rows
+  const long long row_bytes = (long long)H * d * 2;
+  if ((long long)max_seqlen_q * row_bytes >= (1LL << 32) || (long long)max_seqlen_k * row_bytes >= (1LL << 32))
+    return fail(FA_ERR_UNSUPPORTED, "one sequence must span under 4 GiB of rows");
+  // D (fp32 [H, total_q]) takes the dense workspace of one (batch) of total_q rows
+  const size_t need = fa_bwd_workspace_bytes(1, H, total_q);
+  void* ws = workspace;
+  std::unique_lock<std::mutex> ws_lock;   // held through the launch when ws is library-owned
+  if (!workspace) {
+    if (workspace_bytes != 0) return fail(FA_ERR_WORKSPACE, "workspace is NULL but workspace_bytes is not 0");
+    fa_status st = owned_workspace(need, &ws, ws_lock);
+    if (st != FA_OK) return st;
+  } else {
+    if (!aligned16(workspace)) return fail(FA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(FA_ERR_WORKSPACE, "workspace smaller than fa_bwd_workspace_bytes(1, H, total_q)");
+  }
+  fa::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+  a.dsum = static_cast<float*>(ws);
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.B = B; a.H = H; a.N = max_seqlen_q; a.d = d;
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * kLog2e);
+  a.causal = causal ? 1 : 0;
+  a.in_f16 = 0;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.Nk = max_seqlen_k;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  a.stream = stream;
+  hipError_t e = fa::launch_bwd(a);
+  if (e != hipSuccess) return hip_fail(e, "fa_bwd_varlen launch");
+  g_last_error.clear();
+  return FA_OK;
+}
+
 const char* fa_status_string(fa_status s) {
   switch (s) {
     case FA_OK: return "FA_OK";

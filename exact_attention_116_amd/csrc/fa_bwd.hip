@@ -58,20 +58,21 @@ __device__ __forceinline__ int bwd_swz(int r) {
 }
 
 // Direct global->LDS copy of ROWS rows of RB bytes, swizzled; NW waves share
-// the 1 KB instructions.  base_off is the byte offset of the tile's first
-// row in the buffer resource.
+// the 1 KB instructions.  Rows are RG bytes apart in memory (RB for a dense
+// [.., N, d] head, H*d*2 for packed [total, H, d] rows) and RB apart in LDS.
+// base_off is the byte offset of the tile's first row in the buffer resource.
 template <int RB, int ROWS, int NW>
 struct TileLoader {
   static constexpr int NI = ROWS * RB / 1024;
   static constexpr int IPW = NI / NW;
   static_assert(NI % NW == 0, "tile must split evenly over the waves");
   uint32_t goff[IPW];
-  __device__ __forceinline__ void init(int wave, int lane) {
+  __device__ __forceinline__ void init(int wave, int lane, uint32_t RG) {
 #pragma unroll
     for (int x = 0; x < IPW; ++x) {
       const int byte = (wave * IPW + x) * 1024 + lane * 16;
       const int r = byte / RB, p = (byte % RB) / 16;
-      goff[x] = (uint32_t)(r * RB + 16 * (p ^ bwd_swz<RB>(r)));
+      goff[x] = (uint32_t)r * RG + (uint32_t)(16 * (p ^ bwd_swz<RB>(r)));
     }
   }
   __device__ __forceinline__ void load(rsrc_t R, uint32_t base_off, uint8_t* lds, int wave) const {
@@ -122,13 +123,60 @@ struct TileReads {
   }
 };
 
+// Where one (sequence, head) lives.  Dense: [B, H, N, d] tensors, LSE and D
+// [B*H, N].  Packed (cu_q non-null): [total, H, d] token-major rows, LSE and
+// D [H, total_q], sequence b at rows cu_q[b].. (queries) and cu_k[b]..
+// (keys); N and Nk bound the query and key lengths.
+struct BwdLayout {
+  const int* cu_q;
+  const int* cu_k;
+  int H, N, Nk, total_q, total_k;
+};
+
+struct BwdSeq {
+  size_t qbase, kbase, lbase;   // elements: first Q (and dO, O, dQ) row, first K row; LSE/D offset
+  int Lq, Lk, rs;               // lengths, row stride in elements
+};
+
+template <int D, bool PACKED>
+__device__ __forceinline__ BwdSeq bwd_seq(const BwdLayout& lay, int bh) {
+  BwdSeq r;
+  if constexpr (PACKED) {
+    const int b = bh / lay.H, h = bh % lay.H;
+    // the offsets as uniform values (scalar registers: the tile and block
+    // decisions below stay scalar branches), clamped to the tensors, so that
+    // malformed offsets give wrong values, never accesses outside them
+    const int q0 = __builtin_amdgcn_readfirstlane(lay.cu_q[b]);
+    const int q1 = __builtin_amdgcn_readfirstlane(lay.cu_q[b + 1]);
+    const int k0 = __builtin_amdgcn_readfirstlane(lay.cu_k[b]);
+    const int k1 = __builtin_amdgcn_readfirstlane(lay.cu_k[b + 1]);
+    const int sq = min(max(q0, 0), lay.total_q);
+    const int sk = min(max(k0, 0), lay.total_k);
+    r.Lq = min(max(min(q1, lay.total_q) - sq, 0), lay.N);
+    r.Lk = min(max(min(k1, lay.total_k) - sk, 0), lay.Nk);
+    r.rs = lay.H * D;
+    r.qbase = (size_t)sq * r.rs + (size_t)h * D;
+    r.kbase = (size_t)sk * r.rs + (size_t)h * D;
+    r.lbase = (size_t)h * lay.total_q + sq;
+  } else {
+    r.Lq = r.Lk = lay.N;
+    r.rs = D;
+    r.qbase = r.kbase = (size_t)bh * (size_t)lay.N * D;
+    r.lbase = (size_t)bh * lay.N;
+  }
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // 1. D = rowsum(dO * O)
 // ---------------------------------------------------------------------------
+// Rows are contiguous d-element rows of O and dO.  Dense: row r is (b*H+h)*N
+// + n and D goes to dsum[r].  Packed (H > 0): row r is token r/H, head r%H,
+// and D goes to dsum[(r%H) * total_q + r/H] ([H, total_q], the LSE layout).
 template <int D, bool F16>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void fa_bwd_pre_kernel(const bf16* __restrict__ o, const bf16* __restrict__ dout,
-                       float* __restrict__ dsum, long long rows) {
+                       float* __restrict__ dsum, long long rows, int H, int total_q) {
   constexpr int LPR = D / 8;  // lanes per row, 16 bytes each
   const long long row = (long long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
   const int part = threadIdx.x % LPR;
@@ -140,7 +188,10 @@ void fa_bwd_pre_kernel(const bf16* __restrict__ o, const bf16* __restrict__ dout
     for (int w = 0; w < 4; ++w) acc = dot2_16<F16>(a[w], b[w], acc);
   }
   acc = group_sum<LPR>(acc);
-  if (row < rows && part == 0) dsum[row] = acc;
+  if (row < rows && part == 0) {
+    const long long at = H > 0 ? (long long)(row % H) * total_q + row / H : row;
+    dsum[at] = acc;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -175,12 +226,12 @@ __device__ __forceinline__ void lds_barrier() {
 // (-LSE/scale and -D), so P = exp2(c s) and dS = P s without a per-element
 // correction.  Q and dO rows are read row-wise for the first product and
 // through ds_read_b64_tr_b16 for the second.
-template <int D, int BQ, bool CAUSAL, bool F16, int PD = 3>
+template <int D, int BQ, bool CAUSAL, bool F16, bool PACKED, int PD = 3>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512)))
 void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                              const bf16* __restrict__ v, const bf16* __restrict__ dout,
                              const float* __restrict__ lse, const float* __restrict__ dsum,
-                             bf16* __restrict__ dk, bf16* __restrict__ dv, int BH, int N,
+                             bf16* __restrict__ dk, bf16* __restrict__ dv, int BH, BwdLayout lay,
                              float c /* scale*log2(e) */, float scale) {
   constexpr int NW = 8, NP = NW / 2;
   constexpr int RB = D * 2;
@@ -202,36 +253,41 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int l32 = lane & 31, g = lane >> 5;
   const int bh = blockIdx.x % BH;
   const int kt = blockIdx.x / BH;       // heaviest (earliest keys) first under causal
+  const BwdSeq sq = bwd_seq<D, PACKED>(lay, bh);
+  const int Lq = sq.Lq, Lk = sq.Lk;
+  const int rs = PACKED ? sq.rs : D;    // row stride in elements (a constant when dense)
   const int k0 = kt * BC;
+  if (k0 >= Lk) return;                 // past this sequence's keys (whole workgroup)
+  const int off = CAUSAL ? Lk - Lq : 0; // causal: query i sees keys j <= i + off
   const int kw = k0 + pair * 32;        // the pair's first key
   const int my_key = kw + l32;
   const float neg_inv_scale = -1.f / scale;
 
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2u;
-  const rsrc_t Qr = make_rsrc(q + head, head_bytes);
-  const rsrc_t Or = make_rsrc(dout + head, head_bytes);
-  const rsrc_t Lr = make_rsrc(lse + (size_t)bh * N, (uint32_t)N * 4u);
-  const rsrc_t Dr = make_rsrc(dsum + (size_t)bh * N, (uint32_t)N * 4u);
+  const uint32_t RG = (uint32_t)rs * 2u;       // bytes from one row to the next in memory
+  const rsrc_t Qr = make_rsrc(q + sq.qbase, (uint32_t)Lq * RG);
+  const rsrc_t Or = make_rsrc(dout + sq.qbase, (uint32_t)Lq * RG);
+  const rsrc_t Lr = make_rsrc(lse + sq.lbase, (uint32_t)Lq * 4u);
+  const rsrc_t Dr = make_rsrc(dsum + sq.lbase, (uint32_t)Lq * 4u);
 
   bf16x8 kv[D / 16];
   {
-    const rsrc_t R = make_rsrc((role ? v : k) + head, head_bytes);
+    const rsrc_t R = make_rsrc((role ? v : k) + sq.kbase, (uint32_t)Lk * RG);
 #pragma unroll
     for (int u = 0; u < D / 16; ++u)
-      kv[u] = __builtin_bit_cast(bf16x8, buf_load16(R, ((uint32_t)my_key * D + 16 * u + 8 * g) * 2u));
+      kv[u] = __builtin_bit_cast(bf16x8, buf_load16(R, (uint32_t)my_key * RG + (16u * u + 8u * g) * 2u));
   }
 
   TileLoader<RB, BQ, NW> ld;
-  ld.init(wave, lane);
+  ld.init(wave, lane, RG);
   TileReads<D> rd;
   rd.init(lane);
 
-  const int nqt = (N + BQ - 1) / BQ;
-  const int it0 = CAUSAL ? (k0 / BQ) : 0;
+  const int nqt = (Lq + BQ - 1) / BQ;
+  // the first query tile that sees one of this workgroup's keys
+  const int it0 = CAUSAL ? max(k0 - off, 0) / BQ : 0;
   auto load_tile = [&](int it) {
     uint8_t* st = smem + (it & 1) * STAGE;
-    const uint32_t qoff = (uint32_t)it * BQ * RB;
+    const uint32_t qoff = (uint32_t)it * BQ * RG;
     ld.load(Qr, qoff, st, wave);
     ld.load(Or, qoff, st + TILE, wave);
     if (wave < 2 * (BQ / 64)) {           // LSE (even waves) and D (odd), 64 rows each
@@ -305,7 +361,7 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         const int qb0 = it * BQ + 32 * blk;
         uint8_t* pb = smem + 2 * STAGE + ((blk & 1) * NP + pair) * PBLK;
         if constexpr (R == 0) {
-          const bool edge = (CAUSAL && qb0 < kw + 31) || qb0 + 32 > N;
+          const bool edge = (CAUSAL && qb0 + off < kw + 31) || qb0 + 32 > Lq;
           // ---- S - LSE/scale for this block (the accumulator starts at
           // -LSE/scale, so exp2(c * s) is P) ----
           f32x16 s;
@@ -342,8 +398,8 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 float p1 = __builtin_amdgcn_exp2f(s[e + 1] * c);
                 if constexpr (ED) {
                   const int qi = qb0 + 8 * (e >> 2) + 4 * g + (e & 3);
-                  if (qi >= N || (CAUSAL && my_key > qi)) p0 = 0.f;
-                  if (qi + 1 >= N || (CAUSAL && my_key > qi + 1)) p1 = 0.f;
+                  if (qi >= Lq || (CAUSAL && my_key > qi + off)) p0 = 0.f;
+                  if (qi + 1 >= Lq || (CAUSAL && my_key > qi + 1 + off)) p1 = 0.f;
                 }
                 pw[i] = pack16<F16>(p0, p1);
               }
@@ -399,7 +455,9 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       __syncthreads();
     }
 
-    // ---- the last block's deferred second product ----
+    // ---- the last block's deferred second product (none without a query
+    // tile: then dK and dV stay zero) ----
+    if (it0 >= nqt) return;
     if constexpr (R == 0) {
       second(pbo);
     } else {
@@ -420,20 +478,20 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // ---- epilogue: lane holds key my_key, features 32cb + 8(i/4) + 4g + i%4;
   // whole rows of dV (role 0) or dK (role 1) through LDS, 32 rows per wave ----
   static_assert(NW * 32 * RB <= (int)sizeof(smem), "output staging fits the tile buffers");
-  bf16* out = (role ? dk : dv) + (size_t)bh * N * D;
-  store_tile_rows<F16, D>(smem + wave * 32 * RB, acc, role ? scale : 1.f, lane, N - kw,
-                          [&](int r) { return out + (size_t)(kw + r) * D; });
+  bf16* out = (role ? dk : dv) + sq.kbase;
+  store_tile_rows<F16, D>(smem + wave * 32 * RB, acc, role ? scale : 1.f, lane, Lk - kw,
+                          [&](int r) { return out + (size_t)(kw + r) * rs; });
 }
 
 // ---------------------------------------------------------------------------
 // 3. dQ: query tiles outer
 // ---------------------------------------------------------------------------
-template <int D, int BC, int NW, bool CAUSAL, bool F16>
+template <int D, int BC, int NW, bool CAUSAL, bool F16, bool PACKED>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                       const bf16* __restrict__ v, const bf16* __restrict__ dout,
                       const float* __restrict__ lse, const float* __restrict__ dsum,
-                      bf16* __restrict__ dq, int BH, int N, float c, float scale) {
+                      bf16* __restrict__ dq, int BH, BwdLayout lay, float c, float scale) {
   constexpr int RB = D * 2;
   constexpr int BR = NW * 32;           // queries per workgroup
   constexpr int TILE = BC * RB;
@@ -445,47 +503,51 @@ void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: the block skips are scalar branches
   const int l32 = lane & 31, g = lane >> 5;
-  const int nqt = (N + BR - 1) / BR;
   const int bh = blockIdx.x % BH;
+  const BwdSeq sq = bwd_seq<D, PACKED>(lay, bh);
+  const int Lq = sq.Lq, Lk = sq.Lk;
+  const int rs = PACKED ? sq.rs : D;         // row stride in elements (a constant when dense)
+  const int nqt = (Lq + BR - 1) / BR;
   int qt = blockIdx.x / BH;
+  if (qt >= nqt) return;                     // past this sequence's queries (whole workgroup)
   if constexpr (CAUSAL) qt = nqt - 1 - qt;   // longest query tiles first
+  const int off = CAUSAL ? Lk - Lq : 0;      // causal: query i sees keys j <= i + off
   const int q0 = qt * BR;
   const int qw = q0 + wave * 32;
   const int my_q = qw + l32;
 
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2u;
-  const rsrc_t Kr = make_rsrc(k + head, head_bytes);
-  const rsrc_t Vr = make_rsrc(v + head, head_bytes);
+  const uint32_t RG = (uint32_t)rs * 2u;     // bytes from one row to the next in memory
+  const rsrc_t Kr = make_rsrc(k + sq.kbase, (uint32_t)Lk * RG);
+  const rsrc_t Vr = make_rsrc(v + sq.kbase, (uint32_t)Lk * RG);
 
   // Q^T and dO^T of this lane's query as B operands; its LSE (base 2) and D
   bf16x8 qb[D / 16], ob[D / 16];
   float lse2 = 0.f, dd = 0.f;
   {
-    const rsrc_t Qr = make_rsrc(q + head, head_bytes);
-    const rsrc_t Or = make_rsrc(dout + head, head_bytes);
+    const rsrc_t Qr = make_rsrc(q + sq.qbase, (uint32_t)Lq * RG);
+    const rsrc_t Or = make_rsrc(dout + sq.qbase, (uint32_t)Lq * RG);
 #pragma unroll
     for (int u = 0; u < D / 16; ++u) {
-      const uint32_t off = ((uint32_t)my_q * D + 16 * u + 8 * g) * 2u;
-      qb[u] = __builtin_bit_cast(bf16x8, buf_load16(Qr, off));
-      ob[u] = __builtin_bit_cast(bf16x8, buf_load16(Or, off));
+      const uint32_t o16 = (uint32_t)my_q * RG + (16u * u + 8u * g) * 2u;
+      qb[u] = __builtin_bit_cast(bf16x8, buf_load16(Qr, o16));
+      ob[u] = __builtin_bit_cast(bf16x8, buf_load16(Or, o16));
     }
-    if (my_q < N) {
-      lse2 = lse[(size_t)bh * N + my_q] * kLog2e;
-      dd = dsum[(size_t)bh * N + my_q];
+    if (my_q < Lq) {
+      lse2 = lse[sq.lbase + my_q] * kLog2e;
+      dd = dsum[sq.lbase + my_q];
     }
   }
 
   TileLoader<RB, BC, NW> ld;
-  ld.init(wave, lane);
+  ld.init(wave, lane, RG);
   TileReads<D> rd;
   rd.init(lane);
 
-  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
+  const int kv_end = CAUSAL ? min(Lk, max(q0 + BR + off, 0)) : Lk;
   const int ntiles = (kv_end + BC - 1) / BC;
   auto load_tile = [&](int j) {
     uint8_t* st = smem + (j & 1) * STAGE;
-    const uint32_t off = (uint32_t)j * BC * RB;
+    const uint32_t off = (uint32_t)j * BC * RG;
     ld.load(Kr, off, st, wave);
     ld.load(Vr, off, st + TILE, wave);
   };
@@ -507,7 +569,7 @@ void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
     for (int blk = 0; blk < BC / 32; ++blk) {
       const int kb0 = j * BC + 32 * blk;
-      if (CAUSAL && kb0 > qw + 31) continue;   // the block lies above the diagonal
+      if (CAUSAL && kb0 > qw + 31 + off) continue;   // the block lies above the diagonal
       // ---- S^T = K Q^T and dP^T = V dO^T: keys on rows, this lane's query on the column ----
       f32x16 s = f32x16{}, dp = f32x16{};
       {
@@ -525,7 +587,9 @@ void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         }
       }
       // ---- dS^T (row i of the accumulator is key kb0 + 8(i/4) + 4g + i%4) ----
-      const bool edge = (CAUSAL && kb0 + 31 > qw) || kb0 + 32 > N || qw + 32 > N;
+      // (one comparison for both lengths: with separate ones the compiler's
+      // register allocation of this loop spills)
+      const bool edge = (CAUSAL && kb0 + 31 > qw + off) || max(kb0 + 32 - Lk, qw + 32 - Lq) > 0;
       bf16x8 ps[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -539,7 +603,7 @@ void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
             float p = __builtin_amdgcn_exp2f(fmaf(s[i], c, -lse2));
             if (edge) {
               const int key = kb0 + 8 * (i >> 2) + 4 * g + (i & 3);
-              if (key >= N || my_q >= N || (CAUSAL && key > my_q)) p = 0.f;
+              if (key >= Lk || my_q >= Lq || (CAUSAL && key > my_q + off)) p = 0.f;
             }
             dsv[e] = p * (dp[i] - dd);
           }
@@ -569,12 +633,12 @@ void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   // whole dQ rows through LDS, 32 rows per wave
   static_assert(NW * 32 * RB <= (int)sizeof(smem), "output staging fits the tile buffers");
-  store_tile_rows<F16, D>(smem + wave * 32 * RB, acc, scale, lane, N - qw,
-                          [&](int r) { return dq + ((size_t)bh * N + qw + r) * D; });
+  store_tile_rows<F16, D>(smem + wave * 32 * RB, acc, scale, lane, Lq - qw,
+                          [&](int r) { return dq + sq.qbase + (size_t)(qw + r) * rs; });
 }
 
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool F16>
+template <int D, bool CAUSAL, bool F16, bool PACKED>
 static hipError_t launch_bwd_d(const BwdArgs& a) {
   // dK/dV: 128 keys per workgroup (four wave pairs, two waves per SIMD),
   // 128-query tiles (against 64: +3% at N = 16384, causal).
@@ -584,34 +648,43 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
   constexpr int BCQ = 128, NWQ = 8;
   const int BH = a.B * a.H;
   hipStream_t st = (hipStream_t)a.stream;
-  const long long rows = (long long)BH * a.N;
+  const bool packed = PACKED;
+  const BwdLayout lay{a.cu_q, a.cu_k, a.H, a.N, packed ? a.Nk : a.N, a.total_q, a.total_k};
+  // D for every query row: B*H*N dense rows, or total_q*H packed rows
+  const long long rows = packed ? (long long)a.total_q * a.H : (long long)BH * a.N;
   hipLaunchKernelGGL((fa_bwd_pre_kernel<D, F16>), dim3((unsigned)((rows + (256 / (D / 8)) - 1) / (256 / (D / 8)))),
-                     dim3(256), 0, st, (const bf16*)a.o, (const bf16*)a.dout, a.dsum, rows);
+                     dim3(256), 0, st, (const bf16*)a.o, (const bf16*)a.dout, a.dsum, rows,
+                     packed ? a.H : 0, a.total_q);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nkt = (a.N + BCK - 1) / BCK;
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BQ, CAUSAL, F16>), dim3((unsigned)((long long)nkt * BH)),
+  const int nkt = (lay.Nk + BCK - 1) / BCK;   // of the longest key sequence
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BQ, CAUSAL, F16, PACKED>), dim3((unsigned)((long long)nkt * BH)),
                      dim3(NWK * 64), 0, st, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
-                     (const bf16*)a.dout, a.lse, a.dsum, (bf16*)a.dk, (bf16*)a.dv, BH, a.N,
+                     (const bf16*)a.dout, a.lse, a.dsum, (bf16*)a.dk, (bf16*)a.dv, BH, lay,
                      a.scale_log2, a.scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nqt = (a.N + NWQ * 32 - 1) / (NWQ * 32);
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BCQ, NWQ, CAUSAL, F16>), dim3((unsigned)((long long)nqt * BH)),
+  const int nqt = (a.N + NWQ * 32 - 1) / (NWQ * 32);   // of the longest query sequence
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BCQ, NWQ, CAUSAL, F16, PACKED>), dim3((unsigned)((long long)nqt * BH)),
                      dim3(NWQ * 64), 0, st, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
-                     (const bf16*)a.dout, a.lse, a.dsum, (bf16*)a.dq, BH, a.N, a.scale_log2,
+                     (const bf16*)a.dout, a.lse, a.dsum, (bf16*)a.dq, BH, lay, a.scale_log2,
                      a.scale);
   return hipGetLastError();
 }
 
-template <bool F16>
+template <bool F16, bool PACKED>
 static hipError_t launch_bwd_t(const BwdArgs& a) {
-  if (a.d == 128) return a.causal ? launch_bwd_d<128, true, F16>(a) : launch_bwd_d<128, false, F16>(a);
-  return a.causal ? launch_bwd_d<64, true, F16>(a) : launch_bwd_d<64, false, F16>(a);
+  if (a.d == 128)
+    return a.causal ? launch_bwd_d<128, true, F16, PACKED>(a) : launch_bwd_d<128, false, F16, PACKED>(a);
+  return a.causal ? launch_bwd_d<64, true, F16, PACKED>(a) : launch_bwd_d<64, false, F16, PACKED>(a);
 }
 
 hipError_t launch_bwd(const BwdArgs& a) {
-  return a.in_f16 ? launch_bwd_t<true>(a) : launch_bwd_t<false>(a);
+  if (a.cu_q) {   // packed sequences: bf16 only
+    if (a.in_f16) return hipErrorNotSupported;
+    return launch_bwd_t<false, true>(a);
+  }
+  return a.in_f16 ? launch_bwd_t<true, false>(a) : launch_bwd_t<false, false>(a);
 }
 
 }  // namespace fa

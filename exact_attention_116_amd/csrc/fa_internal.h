@@ -64,6 +64,13 @@ struct BwdArgs {
   float scale_log2;
   int causal;
   int in_f16;         // fp16 tensors instead of bf16
+  // packed sequences of unequal lengths (bf16): q, o, dout, dq are
+  // [total_q, H, d], k, v, dk, dv [total_k, H, d], lse and dsum [H, total_q];
+  // sequence b at rows cu_q[b].. and cu_k[b]..  N and Nk bound the query and
+  // key lengths.  Null cu_q: the dense [B, H, N, d] layout.
+  const int* cu_q;
+  const int* cu_k;
+  int Nk, total_q, total_k;
   void* stream;
 };
 

@@ -27,9 +27,9 @@
  *     returns FA_ERR_HIP (fa_last_error() has the HIP text); faults inside a
  *     kernel surface at the caller's next synchronisation.
  *   - Calls that share a library-owned workspace (fa_decode_splitkv, and
- *     fa_decode_splitkv_gqa, fa_decode_splitkv_varlen, fa_bwd or fa_bwd_ex
- *     with a NULL workspace) on one device must not run concurrently on
- *     different streams.  From several host threads on one stream they are
+ *     fa_decode_splitkv_gqa, fa_decode_splitkv_varlen, fa_bwd, fa_bwd_ex or
+ *     fa_bwd_varlen with a NULL workspace) on one device must not run
+ *     concurrently on different streams.  From several host threads on one stream they are
  *     safe: each call queues all of its launches while holding the
  *     workspace lock, so the buffer is neither freed nor shared between
  *     the launches of one call.  Growing that workspace synchronises the
@@ -322,6 +322,37 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
                     const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
                     float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/*
+ * fa_bwd_varlen -- fa_bwd over a batch of packed sequences of unequal
+ * lengths: the gradients of fa_fwd_varlen's output (the Flash Attention
+ * note's "使用注意事项" lifts the power-of-two length rule; the backward
+ * pass is the same recomputation as fa_bwd, per sequence).  Sequence b has
+ * Lq = cu_seqlens_q[b+1] - cu_seqlens_q[b] queries and Lk =
+ * cu_seqlens_k[b+1] - cu_seqlens_k[b] keys.
+ *
+ * q, o, dout, dq : bf16 [total_q, H, d]     k, v, dk, dv : bf16 [total_k, H, d]
+ * lse            : fp32 [H, total_q], fa_fwd_varlen's output for the same
+ *                  q, k, v, offsets, scale and causal flag (o likewise).
+ * cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, causal : as for
+ *          fa_fwd_varlen (masking aligned at the end of each sequence).  A
+ *          query that sees no key gets dQ = 0; keys of a sequence without
+ *          queries get dK = dV = 0.  Rows outside every sequence's range are
+ *          not written.
+ * The workspace holds D (fp32 [H, total_q]): at least
+ * fa_bwd_workspace_bytes(1, H, total_q) bytes, or NULL with
+ * workspace_bytes = 0 for the library-owned workspace (which allocates).
+ * d in {64, 128}, else FA_ERR_UNSUPPORTED; scale finite and > 0; pointers to
+ * tensors 16-byte aligned, offsets 4-byte aligned.  One sequence's rows of
+ * one tensor must span under 4 GiB (max_seqlen * H * d * 2 < 2^32), else
+ * FA_ERR_UNSUPPORTED.  Deterministic (no atomics).
+ */
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H,
+                        int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int d,
+                        float scale, int causal, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /* A static string naming the status. */
 const char* fa_status_string(fa_status s);

@@ -278,6 +278,35 @@ def test_bwd_rejects(lib, kw, status):
     assert fa.fa_bwd_workspace_bytes(1, 2, 100) == 1024   # 800 rounded up to 256
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dv=A + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=A + 4), fa.FA_ERR_INVALID_ARG),
+    (dict(cuq=None), fa.FA_ERR_INVALID_ARG),
+    (dict(cuk=A + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(mk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(tq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(mq=1 << 20, H=32), fa.FA_ERR_UNSUPPORTED),   # 8 GiB of query rows
+    (dict(ws=A, ws_bytes=64), fa.FA_ERR_WORKSPACE),     # smaller than fa_bwd_workspace_bytes(1, H, tq)
+    (dict(ws=None, ws_bytes=64), fa.FA_ERR_WORKSPACE),
+    (dict(ws=A + 8, ws_bytes=1 << 20), fa.FA_ERR_WORKSPACE),
+])
+def test_bwd_varlen_rejects(lib, kw, status):
+    a = dict(q=A, k=A, v=A, o=A, do=A, lse=A, dq=A, dk=A, dv=A, cuq=A, cuk=A, B=2, H=4, mq=64,
+             mk=80, tq=100, tk=150, d=128, scale=0.1, causal=1, ws=A, ws_bytes=1 << 20)
+    a.update(kw)
+    st = lib.fa_bwd_varlen(*[a[x] for x in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "cuq",
+                                            "cuk", "B", "H", "mq", "mk", "tq", "tk", "d", "scale",
+                                            "causal", "ws", "ws_bytes")], None)
+    assert st == status
+    assert fa.fa_last_error() != ""
+    # D takes H * total_q fp32 values: the dense workspace of one batch of total_q rows
+    assert fa.fa_bwd_workspace_bytes(1, 4, 100) == 1792   # 1600 rounded up to 256
+
+
 def test_binding_rejects_host_and_strided_tensors():
     import torch
     x = torch.zeros(1, 1, 16, 128, dtype=torch.bfloat16)

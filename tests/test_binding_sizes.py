@@ -110,6 +110,14 @@ def test_varlen_and_quantize_and_backward_sizes():
     h = lambda: Fake(B * H * N * d, 2, "torch.float16")
     raises_short("dout", fa.fa_bwd_ex, h(), h(), h(), h(), Fake(10, 2, "torch.float16"),
                  Fake(B * H * N, 4), h(), h(), h(), B, H, N, d, 0.1, True, dtype=fa.FA_FP16)
+    # packed backward: q-side tensors hold total_q rows, k-side total_k, lse H * total_q
+    qs, ks = (lambda: Fake(tq * H * d)), (lambda: Fake(tk * H * d))
+    raises_short("dv", fa.fa_bwd_varlen, qs(), ks(), ks(), qs(), qs(), Fake(H * tq, 4), qs(), ks(),
+                 Fake(tk * H * d - 1), cu(B + 1), cu(B + 1), B, H, 30, 40, tq, tk, d, 0.1, True)
+    raises_short("lse", fa.fa_bwd_varlen, qs(), ks(), ks(), qs(), qs(), Fake(H * tq - 1, 4), qs(),
+                 ks(), ks(), cu(B + 1), cu(B + 1), B, H, 30, 40, tq, tk, d, 0.1, True)
+    raises_short("cu_seqlens_q", fa.fa_bwd_varlen, qs(), ks(), ks(), qs(), qs(), Fake(H * tq, 4),
+                 qs(), ks(), ks(), cu(B), cu(B + 1), B, H, 30, 40, tq, tk, d, 0.1, True)
 
 
 def raises_dtype(name, fn, *args, **kw):
@@ -154,3 +162,6 @@ def test_dtypes_are_checked():
     raises_dtype("dq", fa.fa_bwd, t(), t(), t(), t(), t(), f32(rows), f32(full), t(), t(),
                  B, H, N, d, 0.1, True)
     raises_dtype("codes", fa.fa_fp8_quantize, t(), f32(d), Fake(full, 2), f32(nsb), B, H, N, d)
+    raises_dtype("dout", fa.fa_bwd_varlen, ok(), ok(), ok(), ok(), Fake(full, 2, "torch.float16"),
+                 f32(rows), ok(), ok(), ok(), Fake(B + 1, 4, "torch.int32"),
+                 Fake(B + 1, 4, "torch.int32"), B, H, N, N, N, N, d, 0.1, True)
