@@ -17,15 +17,15 @@ One step = one pass of the whole hot path over resident synthetic inputs:
     d=128, each a chunk of new queries against its cached keys, causal
     aligned at the sequence end (FLOPs: 4*d per visible query-key pair)
   * backward (dQ, dK, dV) of the B=2 H=32 N=2048 causal and B=1 H=16 N=16384
-    causal forward passes (FLOPs counted as 2.5x the forward's: five matrix
-    products against two)
+    causal forward passes, and of the ragged chunked prefill (FLOPs counted
+    as 2.5x the forward's: five matrix products against two)
   * fp8 forward, B=4 H=16 N=8192 d=128, causal (when the library has it)
 
 ``value`` is the bf16 causal forward throughput over the N=2048 and N=16384
 workloads (their FLOPs over their summed kernel time, 4*B*H*N^2*d/2 per
 causal call); the decode bandwidth is reported beside it.  Each launch is
 bracketed by HIP events on the stream it runs on.  After the timed steps,
-C3, C2 causal, the ragged prefill and both backward workloads are also timed
+C3, C2 causal, the ragged prefill and the three backward workloads are also timed
 as 20 or more back-to-back launches under one event pair (``steady``): no
 event between launches, and no decode launch letting the clock recover.  The
 CPU oracle is timed on a bounded sample of the same workloads (rank 0, N=1
@@ -191,7 +191,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", default="all",
-                    help="all, or a comma list of: c2c c2n c3 c3h c4 c4s1 c5 q5 c6 c7 c8 b2c b3 "
+                    help="all, or a comma list of: c2c c2n c3 c3h c4 c4s1 c5 q5 c6 c7 c8 b2c b3 b8 "
                          "(profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy per step (for HBM counter scaling)")
@@ -306,28 +306,29 @@ def main():
         nq = xq[0].numel()
         jobs.append(("q5", runq5, 0.0, 3 * nq * 3 + 3 * sq5[0].numel() * 4, "quant"))
 
-    if want("c8"):
-        wv = fi.VARLEN_PREFILL
-        log(f"generating ragged prefill inputs ({len(wv['lq'])} sequences)")
-        Hv, dv_ = wv["H"], wv["d"]
+    wv = fi.VARLEN_PREFILL
+    Hv, dv_ = wv["H"], wv["d"]
+    # visible pairs of the ragged batch: query i of a chunk sees min(Lk, i + 1 + Lk - Lq) keys
+    pairs = sum(sum(min(lk, i + 1 + lk - lq) for i in range(lq))
+                for lq, lk in zip(wv["lq"], wv["lk"]))
 
-        def packed(tensor, lens):
-            out = np.empty((int(sum(lens)), Hv, dv_), dtype=np.uint16)
-            r = 0
-            for b, n in enumerate(lens):
-                for h in range(Hv):
-                    out[r:r + n, h] = fi.bf16_slice(wv["wid"], tensor, b, h, n, dv_)
-                r += n
-            return up_bf16(out)
+    def packed(tensor, lens):
+        out = np.empty((int(sum(lens)), Hv, dv_), dtype=np.uint16)
+        r = 0
+        for b, n in enumerate(lens):
+            for h in range(Hv):
+                out[r:r + n, h] = fi.bf16_slice(wv["wid"], tensor, b, h, n, dv_)
+            r += n
+        return up_bf16(out)
+
+    if want("c8"):
+        log(f"generating ragged prefill inputs ({len(wv['lq'])} sequences)")
         q8 = packed(fi.Q_ID, wv["lq"])
         k8, v8 = packed(fi.K_ID, wv["lk"]), packed(fi.V_ID, wv["lk"])
         o8 = torch.empty_like(q8)
         l8 = torch.empty((Hv, q8.shape[0]), dtype=torch.float32, device=dev)
         cq8 = torch.tensor(np.concatenate([[0], np.cumsum(wv["lq"])]), dtype=torch.int32, device=dev)
         ck8 = torch.tensor(np.concatenate([[0], np.cumsum(wv["lk"])]), dtype=torch.int32, device=dev)
-        # visible pairs: query i of a chunk sees min(Lk, i + 1 + Lk - Lq) keys
-        pairs = sum(sum(min(lk, i + 1 + lk - lq) for i in range(lq))
-                    for lq, lk in zip(wv["lq"], wv["lk"]))
         jobs.append(("c8", lambda: fa.fa_fwd_varlen(
             q8, k8, v8, o8, l8, cq8, ck8, len(wv["lq"]), Hv, max(wv["lq"]), max(wv["lk"]),
             q8.shape[0], k8.shape[0], dv_, dv_ ** -0.5, True, stream=stream),
@@ -352,6 +353,27 @@ def main():
                            fa.fa_bwd(q, k, v, o, do, l, gr[0], gr[1], gr[2], w.B, w.H, w.N, w.d,
                                      w.scale, True, ws, nb, stream=stream)),
                      2.5 * fwd_flops(wb, True), 8 * wb.B * wb.H * wb.N * wb.d * 2, "bwd_bf16"))
+
+    if want("b8"):
+        log("generating ragged prefill backward inputs")
+        qr, dor = packed(fi.Q_ID, wv["lq"]), packed(fi.DO_ID, wv["lq"])
+        kr, vr = packed(fi.K_ID, wv["lk"]), packed(fi.V_ID, wv["lk"])
+        tq, tk, nseq = qr.shape[0], kr.shape[0], len(wv["lq"])
+        orr = torch.empty_like(qr)
+        lr = torch.empty((Hv, tq), dtype=torch.float32, device=dev)
+        cqr = torch.tensor(np.concatenate([[0], np.cumsum(wv["lq"])]), dtype=torch.int32, device=dev)
+        ckr = torch.tensor(np.concatenate([[0], np.cumsum(wv["lk"])]), dtype=torch.int32, device=dev)
+        mq, mk = max(wv["lq"]), max(wv["lk"])
+        fa.fa_fwd_varlen(qr, kr, vr, orr, lr, cqr, ckr, nseq, Hv, mq, mk, tq, tk, dv_, dv_ ** -0.5,
+                         True, stream=stream)
+        gr_ = [torch.empty_like(qr), torch.empty_like(kr), torch.empty_like(vr)]
+        wsr_b = fa.fa_bwd_workspace_bytes(1, Hv, tq)
+        wsr = torch.empty(wsr_b // 4, dtype=torch.float32, device=dev)
+        jobs.append(("b8", lambda: fa.fa_bwd_varlen(
+            qr, kr, vr, orr, dor, lr, gr_[0], gr_[1], gr_[2], cqr, ckr, nseq, Hv, mq, mk, tq, tk,
+            dv_, dv_ ** -0.5, True, wsr, wsr_b, stream=stream),
+            2.5 * 4.0 * dv_ * Hv * pairs, (4 * qr.numel() + 4 * kr.numel()) * 2 + lr.numel() * 4,
+            "bwd_bf16"))
 
     def fp8_built():
         t = torch.zeros((1, 1, 64, 128), dtype=torch.uint8, device=dev)
@@ -425,7 +447,7 @@ def main():
     # their in-step time.  C3's figure is the roofline's `steady`; the others
     # sit beside their workloads.
     steady_of = {}
-    for sname in ("c3", "c2c", "c8", "b2c", "b3"):
+    for sname in ("c3", "c2c", "c8", "b2c", "b3", "b8"):
         job = next((j for j in jobs if j[0] == sname), None)
         if job is None:
             continue
@@ -536,10 +558,12 @@ def main():
                               "frac": g / PEAK_HBM_GBS, "traffic": None,
                               "algorithmic_bytes": res["q5"]["bytes"]}}
     backward = {}
-    for tag in ("b2c", "b3"):
+    for tag in ("b2c", "b3", "b8"):
         if tag in res:
             a = res[tag]["tflops"]
-            backward[tag] = {"workload": fi.WORKLOADS[2 if tag == "b2c" else 3].name + " causal",
+            wname = (fi.VARLEN_PREFILL["name"] if tag == "b8"
+                     else fi.WORKLOADS[2 if tag == "b2c" else 3].name) + " causal"
+            backward[tag] = {"workload": wname,
                              "value": a, "unit": "TFLOPS", "ms": res[tag]["ms_mean"],
                              "roofline": {"kernel": "fa_bwd_pre_kernel + fa_bwd_dkdv_kernel + "
                                                     "fa_bwd_dq_kernel",
@@ -575,7 +599,8 @@ def main():
         "config": {"workload": "bf16 causal fwd B2H32N2048d128 + B1H16N16384d128 "
                                "(value); split-KV decode B8H32Lkv65536d128 S64 (decode); "
                                "grouped decode B8 Hq64/Hkv8 and Hq32/Hkv1 Lkv65536 (decode_gqa); "
-                               "causal backward of B2H32N2048d128 and B1H16N16384d128 (backward); "
+                               "causal backward of B2H32N2048d128, B1H16N16384d128 and of the "
+                               "ragged chunked prefill (backward); "
                                "ragged chunked prefill of 8 packed sequences H32d128 (varlen_prefill); "
                                "bf16->fp8 quantisation of the fp8 workload (fp8_quantize); "
                                "fp16 causal fwd B1H16N16384d128 (fp16_prefill)",

@@ -569,7 +569,8 @@ void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
     for (int blk = 0; blk < BC / 32; ++blk) {
       const int kb0 = j * BC + 32 * blk;
-      if (CAUSAL && kb0 > qw + 31 + off) continue;   // the block lies above the diagonal
+      // the wave is past its sequence's queries, or the block lies above the diagonal
+      if (qw >= Lq || (CAUSAL && kb0 > qw + 31 + off)) continue;
       // ---- S^T = K Q^T and dP^T = V dO^T: keys on rows, this lane's query on the column ----
       f32x16 s = f32x16{}, dp = f32x16{};
       {

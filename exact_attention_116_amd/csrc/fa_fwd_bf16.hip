@@ -241,7 +241,8 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       loaded = more;
 
       const int kb = j * BC;
-      const bool active = !CAUSAL || kb <= qw + 31 + off;
+      // a wave past its sequence's queries, or wholly before this tile's keys, skips the math
+      const bool active = qw < Lq && (!CAUSAL || kb <= qw + 31 + off);
       if (active) {
         const bf16* Ks = smem + buf * (C::KTILE + C::VTILE);
         const bf16* Vs = Ks + C::KTILE;
