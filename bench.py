@@ -59,13 +59,13 @@ PEAK_HBM_GBS = 8000.0
 # split-merge kernel's counters to the split kernel's.
 COUNTER_SCALE = {"fetch": 1048576.0 / 524306.0, "write": 1.0}
 TRAFFIC_KIB = {
-    "c3": {"src": ["fa_fwd_bf16.hip"], "fetch_kib": 211522.9, "write_kib": 68608.0,
-           "sha256": "12aac91df1f600d802e5741b2944d89b73768addfba3dd87ea15de24c66e5242"},
-    "c4": {"src": ["fa_decode.hip"], "fetch_kib": 4198850.3, "write_kib": 8778.0,
+    "c3": {"src": ["fa_fwd_bf16.hip"], "fetch_kib": 221965.2, "write_kib": 68608.0,
+           "sha256": "accc1a5b37879305a9d781e6f55e41f204d819c1335a16a5b057084035a8686b"},
+    "c4": {"src": ["fa_decode.hip"], "fetch_kib": 4198860.1, "write_kib": 8777.4,
            "sha256": "5e97611a26ac2cfece3c36bca4885bf4a61a66ef052765835b53367d362e873e"},
-    "c6": {"src": ["fa_decode_gqa.hip", "fa_decode.hip"], "fetch_kib": 1057821.5, "write_kib": 17681.8,
+    "c6": {"src": ["fa_decode_gqa.hip", "fa_decode.hip"], "fetch_kib": 1057830.2, "write_kib": 17682.3,
            "sha256": "5173b008bb12a55976be3113d7be1d4c27cdcd419827915ad4c16c6113ac15a9"},
-    "c7": {"src": ["fa_decode_gqa.hip", "fa_decode.hip"], "fetch_kib": 135573.1, "write_kib": 8777.5,
+    "c7": {"src": ["fa_decode_gqa.hip", "fa_decode.hip"], "fetch_kib": 135572.7, "write_kib": 8779.1,
            "sha256": "5173b008bb12a55976be3113d7be1d4c27cdcd419827915ad4c16c6113ac15a9"},
 }
 
