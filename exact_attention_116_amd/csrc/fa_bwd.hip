@@ -16,6 +16,13 @@
 // IEEE fp16 tensors (F16) take the same kernels with the fp16 MFMA and fp16
 // roundings of P and dS; the statistics stay fp32.
 //
+// Packed batches of unequal lengths (PACKED instances) use the same kernels
+// with runtime row strides: [total, H, d] rows, LSE and D as [H, total_q],
+// each workgroup's sequence found from the cumulative lengths, and causal
+// masking aligned at the sequence end (query i sees key j iff
+// j <= i + Lk - Lq).  A query that sees no key gets dQ = 0; keys of a
+// sequence without queries get dK = dV = 0.
+//
 // Three kernels, none of which needs atomics (so the result is
 // deterministic):
 //  1. fa_bwd_pre_kernel: D per query row, fp32, from bf16 O and dO.
