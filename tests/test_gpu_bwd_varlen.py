@@ -142,3 +142,27 @@ def test_bwd_varlen_ragged_prefill_workload(gpu_lib):
     got_sub = [dev_to_f64(g)[:, heads] for g in got]
     check(got_sub, ref, f"{wv['name']} heads {heads}")
     check_zeros(got, lq, lk, True)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_bwd_varlen_random_length_mixes(gpu_lib, seed):
+    """Seeded random batches: 1-6 sequences of 0-700 queries and 0-900 keys
+    (at least one of each overall), H in {1, 2, 5}, d in {64, 128}, causal or
+    not."""
+    fa = gpu_lib
+    rng = np.random.default_rng(9200 + seed)
+    B = int(rng.integers(1, 7))
+    while True:
+        lq = [int(x) for x in rng.integers(0, 701, B)]
+        lk = [int(x) for x in rng.integers(0, 901, B)]
+        if sum(lq) > 0 and sum(lk) > 0:
+            break
+    H = int(rng.choice([1, 2, 5]))
+    d = int(rng.choice([64, 128]))
+    causal = bool(rng.integers(0, 2))
+    wid = 9300 + seed
+    say(f"bwd varlen random lq={lq} lk={lk} H={H} d={d} causal={causal} seed-id={wid}")
+    bits, got, scale = run(fa, lq, lk, H, d, causal, wid, own_ws=bool(seed % 2))
+    ref = reference(bits, lq, lk, scale, causal)
+    check(got, ref, f"random {seed}")
+    check_zeros(got, lq, lk, causal)
