@@ -103,6 +103,13 @@ def fwd_flops(w, causal):
     return f / 2 if causal else f
 
 
+def varlen_pairs(lq, lk):
+    """Visible (query, key) pairs of a packed causal batch: query i of a
+    sequence with Lq queries and Lk keys sees min(Lk, i + 1 + Lk - Lq) keys
+    (end-aligned; none when that is negative)."""
+    return sum(sum(max(0, min(k, i + 1 + k - q)) for i in range(q)) for q, k in zip(lq, lk))
+
+
 def fwd_bytes(w, in_bytes=2, out_bytes=2):
     n = w.B * w.H * w.N * w.d
     return 3 * n * in_bytes + n * out_bytes + w.B * w.H * w.N * 4
@@ -308,9 +315,7 @@ def main():
 
     wv = fi.VARLEN_PREFILL
     Hv, dv_ = wv["H"], wv["d"]
-    # visible pairs of the ragged batch: query i of a chunk sees min(Lk, i + 1 + Lk - Lq) keys
-    pairs = sum(sum(min(lk, i + 1 + lk - lq) for i in range(lq))
-                for lq, lk in zip(wv["lq"], wv["lk"]))
+    pairs = varlen_pairs(wv["lq"], wv["lk"])   # FLOPs: 4*d per visible pair and head
 
     def packed(tensor, lens):
         out = np.empty((int(sum(lens)), Hv, dv_), dtype=np.uint16)

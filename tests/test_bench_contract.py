@@ -35,6 +35,17 @@ def test_prefill_bytes():
     assert bench.fwd_bytes(W[5], in_bytes=1) + 98_304 == 337_739_776
 
 
+def test_ragged_prefill_pairs():
+    # chunk of Lq queries against Lk >= Lq keys, end-aligned causal: Lq*Lk - Lq(Lq-1)/2 pairs
+    assert bench.varlen_pairs([3], [3]) == 6
+    assert bench.varlen_pairs([2], [5]) == 9             # 4 + 5
+    assert bench.varlen_pairs([5], [2]) == 3             # 0, 0, 0, 1, 2: the first three see no key
+    # the ragged prefill batch: 2098176 + 1573376 + 2228480 + 1568896 + 1966848 + 1868160
+    # + 1040448 + 2067300
+    v = fi.VARLEN_PREFILL
+    assert bench.varlen_pairs(v["lq"], v["lk"]) == 14_411_684
+
+
 def test_decode_bytes():
     assert bench.decode_bytes(W[4]) == 8_590_065_664     # K+V 8 589 934 592 + q + o 131 072
     assert bench.decode_bytes(W[6]) == 2_147_745_792     # 8 K/V heads; q, o over 64 query heads
