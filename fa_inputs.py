@@ -12,7 +12,9 @@ does:
 * for the fp8 workload, injects x20 outliers with probability 1e-3 per element
   (each tensor has its own mask stream) and quantises to OCP FP8 E4M3FN codes
   with one float32 scale per 64 consecutive sequence rows of each (b, h),
-  ``scale = amax / 448``, ``code = round_to_nearest_even_saturating(x / scale)``.
+  ``scale = amax / 448`` for Q and K, the smallest power of two with
+  ``amax / scale <= 448`` for V, and
+  ``code = round_to_nearest_even_saturating(x / scale)``.
 
 Workload shapes follow the configurations the kernels are measured on (see
 ``WORKLOADS``).  Attention is defined per (batch, head) on ``[B, H, N, d]``
@@ -33,6 +35,10 @@ OUTLIER_MASK_ID = {Q_ID: 3, K_ID: 4, V_ID: 5}
 DO_ID = 6          # the upstream gradient dO of a backward pass
 SIGNS_ID = 7       # the random signs of an incoherent rotation
 FP8_BLOCK_ROWS = 64
+# V's block scales are powers of two (the E8M0 form of the matrix cores'
+# operand scale); Q's and K's are amax / 448, which keeps a block's largest
+# element exact
+FP8_POW2_SCALE = {Q_ID: False, K_ID: False, V_ID: True}
 E4M3_MAX = 448.0
 
 
@@ -74,7 +80,8 @@ WORKLOADS = {
                 note="one query per (b,h), 64 KiB-key cache, 64 splits"),
     5: Workload(5, "fp8_causal_b4h16n8192d128", "fwd_fp8", 4, 16, 8192, 128,
                 causal=(True,), out_dtype="bf16",
-                note="e4m3 Q/K/V, one fp32 scale per 64 rows per head, 0.1% x20 outliers"),
+                note="e4m3 Q/K/V, one fp32 scale per 64 rows per head (V's powers of two), "
+                     "0.1% x20 outliers"),
     6: Workload(6, "decode_gqa_b8hq64hkv8lkv65536d128s64", "decode_gqa", 8, 64, 1, 128,
                 Lkv=65536, num_splits=64, Hkv=8, causal=(False,), out_dtype="bf16",
                 note="grouped K/V heads (8 query heads per K/V head), 64 KiB-key cache"),
@@ -178,12 +185,21 @@ def f64_to_e4m3fn_codes(y: np.ndarray) -> np.ndarray:
     return codes
 
 
-def quantize_e4m3_rows(x: np.ndarray, block: int = FP8_BLOCK_ROWS):
+def pow2_scale(amax: float) -> float:
+    """The smallest power of two s with amax / s <= 448, from the binary
+    exponent: amax = f * 2^e with f in [0.5, 1) and 448 = 0.875 * 2^9, so
+    s = 2^(e - 9) when f <= 0.875, else 2^(e - 8)."""
+    f, e = np.frexp(np.float64(amax))
+    return float(np.ldexp(1.0, int(e) - 9 if f <= 0.875 else int(e) - 8))
+
+
+def quantize_e4m3_rows(x: np.ndarray, block: int = FP8_BLOCK_ROWS, pow2: bool = False):
     """Quantise one (b, h) slice ``x`` float32 [N, d] with per-``block``-row scales.
 
     Returns (codes uint8 [N, d], scales float32 [ceil(N/block)]).
-    ``scale = amax/448`` in float32 (1.0 for an all-zero block); each element
-    is encoded from ``x / scale`` evaluated in float64.
+    ``scale = amax/448`` in float32, or with ``pow2`` the smallest power of
+    two with amax / scale <= 448 (1.0 for an all-zero block either way); each
+    element is encoded from ``x / scale`` evaluated in float64.
     """
     N, d = x.shape
     nb = (N + block - 1) // block
@@ -192,7 +208,12 @@ def quantize_e4m3_rows(x: np.ndarray, block: int = FP8_BLOCK_ROWS):
     for i in range(nb):
         blk = x[i * block:(i + 1) * block]
         amax = np.float32(np.max(np.abs(blk))) if blk.size else np.float32(0)
-        s = np.float32(amax / np.float32(E4M3_MAX)) if amax > 0 else np.float32(1.0)
+        if amax == 0:
+            s = np.float32(1.0)
+        elif pow2:
+            s = np.float32(pow2_scale(amax))
+        else:
+            s = np.float32(amax / np.float32(E4M3_MAX))
         scales[i] = s
         codes[i * block:(i + 1) * block] = f64_to_e4m3fn_codes(
             blk.astype(np.float64) / np.float64(s))
@@ -236,13 +257,14 @@ def f16_tensor(wid: int, tensor_id: int, B: int, H: int, rows: int, d: int) -> n
 
 
 def fp8_slice(wid: int, tensor_id: int, b: int, h: int, rows: int, d: int,
-              outlier_p: float = 1e-3, outlier_mult: float = 20.0):
-    """One (b, h) of an fp8 workload tensor: (codes [rows, d], scales [ceil(rows/64)])."""
+              outlier_p: float = 1e-3, outlier_mult: float = 20.0, pow2: bool | None = None):
+    """One (b, h) of an fp8 workload tensor: (codes [rows, d], scales [ceil(rows/64)]).
+    ``pow2`` None takes the tensor's rule from FP8_POW2_SCALE."""
     x = normals(wid, tensor_id, b, h, rows, d)
     if outlier_p > 0:
         m = stream(wid, OUTLIER_MASK_ID[tensor_id], b, h).random(size=(rows, d)) < outlier_p
         x[m] *= np.float32(outlier_mult)
-    return quantize_e4m3_rows(x)
+    return quantize_e4m3_rows(x, pow2=FP8_POW2_SCALE[tensor_id] if pow2 is None else pow2)
 
 
 def outlier_bf16_tensor(wid: int, tensor_id: int, B: int, H: int, rows: int, d: int,
@@ -271,7 +293,7 @@ def rotation_signs(wid: int, d: int) -> np.ndarray:
 
 
 def fp8_tensor(wid: int, tensor_id: int, B: int, H: int, rows: int, d: int,
-               outlier_p: float = 1e-3, outlier_mult: float = 20.0):
+               outlier_p: float = 1e-3, outlier_mult: float = 20.0, pow2: bool | None = None):
     """(codes uint8 [B,H,rows,d], scales float32 [B,H,ceil(rows/64)])."""
     nb = (rows + FP8_BLOCK_ROWS - 1) // FP8_BLOCK_ROWS
     codes = np.empty((B, H, rows, d), dtype=np.uint8)
@@ -280,7 +302,7 @@ def fp8_tensor(wid: int, tensor_id: int, B: int, H: int, rows: int, d: int,
     def fill(bh):
         b, h = divmod(bh, H)
         codes[b, h], scales[b, h] = fp8_slice(wid, tensor_id, b, h, rows, d,
-                                              outlier_p, outlier_mult)
+                                              outlier_p, outlier_mult, pow2)
 
     with ThreadPoolExecutor(_workers()) as ex:
         list(ex.map(fill, range(B * H)))

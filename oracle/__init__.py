@@ -25,7 +25,8 @@ attention   the plain definition O = softmax(scale*Q*K^T)*V with its
             yardstick for an fp8 kernel's mean error).
 rotation    incoherent processing for fp8: the random-sign Walsh-Hadamard
             rotation of Q and K along the head dimension, and 64-row block
-            quantisation to E4M3FN.
+            quantisation to E4M3FN with a scale of max|x| / 448 or the
+            smallest power of two that keeps max|x| / scale <= 448.
 
 Every function is pinned by ``tests/test_oracle*.py`` against brute force,
 a library routine (torch's float64 scaled-dot-product attention on the CPU)
@@ -39,4 +40,6 @@ from .attention import (  # noqa: F401
     attention_varlen,
     decode_attention_ragged,
 )
-from .rotation import hadamard_matrix, incoherent_rotation, quantize_e4m3_blocks  # noqa: F401
+from .rotation import (  # noqa: F401
+    hadamard_matrix, incoherent_rotation, quantize_e4m3_blocks, smallest_pow2_scale,
+)

@@ -807,6 +807,56 @@ def test_rotation_preserves_scores_and_spreads_outliers():
     np.testing.assert_allclose(L1, L2, rtol=0, atol=1e-12)
 
 
+def test_pow2_block_scale_is_the_smallest_power_of_two():
+    """The power-of-two scale against a search over exponents: the smallest k
+    with amax <= 448 * 2^k, at random magnitudes and at the boundaries
+    448 * 2^k and one ulp either side of them."""
+    rng = np.random.default_rng(87)
+    amaxes = list(np.exp(rng.uniform(-60, 60, 300)))
+    for k in (-20, -3, 0, 1, 7):
+        b = 448.0 * 2.0 ** k
+        amaxes += [b, np.nextafter(b, 0), np.nextafter(b, np.inf)]
+    amaxes += [2.0 ** -130, 1.0, 224.0, 448.0, 449.0, 1e30]
+    for a in amaxes:
+        s = oracle.smallest_pow2_scale(a)
+        k = next(k for k in range(-200, 200) if a <= 448.0 * 2.0 ** k)
+        assert s == 2.0 ** k, (a, s, k)
+        assert 224.0 < a / s <= 448.0
+        assert s == fi.pow2_scale(a)           # the generator's bit-field rule
+    # the boundaries themselves
+    assert oracle.smallest_pow2_scale(448.0) == 1.0
+    assert oracle.smallest_pow2_scale(np.nextafter(448.0, np.inf)) == 2.0
+    assert oracle.smallest_pow2_scale(224.0) == 0.5
+
+
+def test_pow2_block_quantisation():
+    """With power-of-two scales x / scale is exact, so the oracle and the
+    generator's quantiser agree on every code; each block's largest ratio lies
+    in (224, 448] and every value is within half an E4M3FN step."""
+    rng = np.random.default_rng(89)
+    x = rng.standard_normal((300, 64)).astype(np.float32)
+    x[rng.random(x.shape) < 1e-3] *= 20
+    x[128:192] = 0.0                                   # an all-zero block
+    x[192:256] *= np.float32(2.0 ** -40)               # a tiny block
+    vals, scales, ratio = oracle.quantize_e4m3_blocks(x, pow2=True)
+    codes, gscales = fi.quantize_e4m3_rows(x, pow2=True)
+    np.testing.assert_array_equal(scales, gscales.astype(np.float64))
+    assert scales[2] == 1.0
+    np.testing.assert_array_equal(oracle.round_to_e4m3fn(ratio), oracle.decode_e4m3fn(codes))
+    for i in (0, 1, 3, 4):
+        r = np.abs(ratio[i * 64:(i + 1) * 64]).max()
+        assert 224.0 < r <= 448.0
+        m, _ = np.frexp(scales[i])
+        assert m == 0.5
+    err = np.abs(vals - x)
+    step = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ratio), 2.0 ** -6))) - 3)
+    assert np.all(err <= 0.5 * step * scales[np.arange(300) // 64][:, None] * (1 + 1e-12))
+    # amax / 448 scales on the same data: a different rule, different scales
+    _, s448, _ = oracle.quantize_e4m3_blocks(x)
+    assert np.all(s448[[0, 1, 3, 4]] <= scales[[0, 1, 3, 4]])
+    assert np.all(scales[[0, 1, 3, 4]] < 2 * s448[[0, 1, 3, 4]])
+
+
 def test_block_quantisation_matches_the_generator_quantiser():
     """Two independent E4M3FN quantisers (grid search here, bit arithmetic in
     the input generator) agree except where x/scale is a rounding tie."""
