@@ -11,15 +11,17 @@ One step = one pass of the whole hot path over resident synthetic inputs:
   * split-KV decode with grouped K/V heads, B=8 Lkv=65536 d=128, 64 splits:
     Hq=64 over Hkv=8 (GQA), and Hq=32 over one K/V head (MQA)
   * bf16 -> block-scaled fp8 quantisation of the fp8 workload's Q and K
-    (with the incoherent Hadamard rotation) and V, the input pass of the fp8
-    forward from bf16 activations (HBM-bound: 2 bytes read, 1 written)
+    (with the incoherent Hadamard rotation) and V (power-of-two scales), the
+    input pass of the fp8 forward from bf16 activations (HBM-bound: 2 bytes
+    read, 1 written)
   * ragged chunked prefill: 8 packed sequences of unequal lengths, H=32,
     d=128, each a chunk of new queries against its cached keys, causal
     aligned at the sequence end (FLOPs: 4*d per visible query-key pair)
   * backward (dQ, dK, dV) of the B=2 H=32 N=2048 causal and B=1 H=16 N=16384
     causal forward passes, and of the ragged chunked prefill (FLOPs counted
     as 2.5x the forward's: five matrix products against two)
-  * fp8 forward, B=4 H=16 N=8192 d=128, causal (when the library has it)
+  * fp8 forward, B=4 H=16 N=8192 d=128, causal (when the library has it),
+    V with power-of-two block scales, and again with max|x| / 448 V scales
 
 ``value`` is the bf16 causal forward throughput over the N=2048 and N=16384
 workloads (their FLOPs over their summed kernel time, 4*B*H*N^2*d/2 per
@@ -198,7 +200,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", default="all",
-                    help="all, or a comma list of: c2c c2n c3 c3h c4 c4s1 c5 q5 c6 c7 c8 b2c b3 b8 "
+                    help="all, or a comma list of: c2c c2n c3 c3h c4 c4s1 c5 c5a q5 c6 c7 c8 b2c b3 b8 "
                          "(profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy per step (for HBM counter scaling)")
@@ -309,7 +311,8 @@ def main():
         def runq5():
             for i, x in enumerate(xq):
                 fa.fa_fp8_quantize(x, sg5 if i < 2 else None, cq5[i], sq5[i], w5.B, w5.H, w5.N,
-                                   w5.d, stream=stream)
+                                   w5.d, stream=stream,
+                                   scale_rule=fa.FA_FP8_SCALE_POW2 if i == 2 else None)
         nq = xq[0].numel()
         jobs.append(("q5", runq5, 0.0, 3 * nq * 3 + 3 * sq5[0].numel() * 4, "quant"))
 
@@ -412,6 +415,18 @@ def main():
             torch.cuda.synchronize()
             n5 = w5.B * w5.H * w5.N
             jobs.append(("c5", run5, fwd_flops(w5, True),
+                         3 * n5 * w5.d + 3 * n5 // 64 * 4 + n5 * w5.d * 2 + n5 * 4, "fwd_fp8"))
+            # the same codes of Q and K, V quantised with max|x| / 448 scales,
+            # whose mantissas differ between blocks
+            c, s = fi.fp8_tensor(w5.wid, fi.V_ID, w5.B, w5.H, w5.N, w5.d, pow2=False)
+            x["va"] = torch.from_numpy(c).to(dev)
+            x["vas"] = torch.from_numpy(s).to(dev)
+
+            def run5a():
+                fa.fa_fwd_ex(x["q"], x["k"], x["va"], o5, l5, w5.B, w5.H, w5.N, w5.d, w5.scale,
+                             True, in_dtype=fa.FA_FP8_E4M3, q_scale=x["qs"], k_scale=x["ks"],
+                             v_scale=x["vas"], stream=stream)
+            jobs.append(("c5a", run5a, fwd_flops(w5, True),
                          3 * n5 * w5.d + 3 * n5 // 64 * 4 + n5 * w5.d * 2 + n5 * 4, "fwd_fp8"))
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -562,6 +577,18 @@ def main():
                               "achieved": g, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                               "frac": g / PEAK_HBM_GBS, "traffic": None,
                               "algorithmic_bytes": res["q5"]["bytes"]}}
+    fp8 = None
+    if "c5" in res:
+        a = res["c5"]["tflops"]
+        fp8 = {"workload": w5.name + " causal, V block scales powers of two", "value": a,
+               "unit": "TFLOPS", "ms": res["c5"]["ms_mean"],
+               "amax_v_scales": ({"value": res["c5a"]["tflops"], "ms": res["c5a"]["ms_mean"]}
+                                 if "c5a" in res else None),
+               "roofline": {"kernel": "fa_fwd_fp8_dl_kernel", "bound": "mfma", "achieved": a,
+                            "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                            "frac": a / PEAK_FP8_TFLOPS, "traffic": traffic_bytes("c5"),
+                            "traffic_source": traffic_source("c5"),
+                            "algorithmic_bytes": res["c5"]["bytes"]}}
     backward = {}
     for tag in ("b2c", "b3", "b8"):
         if tag in res:
@@ -608,7 +635,8 @@ def main():
                                "ragged chunked prefill (backward); "
                                "ragged chunked prefill of 8 packed sequences H32d128 (varlen_prefill); "
                                "bf16->fp8 quantisation of the fp8 workload (fp8_quantize); "
-                               "fp16 causal fwd B1H16N16384d128 (fp16_prefill)",
+                               "fp16 causal fwd B1H16N16384d128 (fp16_prefill); "
+                               "fp8 causal fwd B4H16N8192d128 (fp8_forward)",
                    "only": args.only},
         "roofline": roof,
         "decode": decode,
@@ -616,6 +644,7 @@ def main():
         "varlen_prefill": varlen,
         "fp8_quantize": quant,
         "fp16_prefill": fp16,
+        "fp8_forward": fp8,
         "backward": backward or None,
         "workloads": res,
         "device": {"name": prop.name, "cus": prop.multi_processor_count,

@@ -14,12 +14,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
 FA_BF16, FA_FP32, FA_FP8_E4M3, FA_FP16 = range(4)
+FA_FP8_SCALE_AMAX, FA_FP8_SCALE_POW2 = range(2)
 FA_DECODE_SCRATCH_BYTES = 32 << 20   # the fixed scratch of fa_decode_splitkv_noalloc
 
 EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_decode_splitkv", "fa_decode_workspace_bytes",
            "fa_decode_splitkv_ex", "fa_decode_splitkv_noalloc", "fa_decode_splitkv_gqa",
            "fa_decode_splitkv_varlen",
-           "fa_fwd_varlen", "fa_fp8_quantize",
+           "fa_fwd_varlen", "fa_fp8_quantize", "fa_fp8_quantize_ex",
            "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_ex", "fa_bwd_varlen",
            "fa_status_string", "fa_last_error")
 
@@ -73,6 +74,8 @@ def load(path: str | None = None):
     lib.fa_fwd_varlen.restype = I
     lib.fa_fp8_quantize.argtypes = [P, P, P, P, I, I, I, I, P]
     lib.fa_fp8_quantize.restype = I
+    lib.fa_fp8_quantize_ex.argtypes = [P, P, P, P, I, I, I, I, I, P]
+    lib.fa_fp8_quantize_ex.restype = I
     lib.fa_bwd_workspace_bytes.argtypes = [I, I, I]
     lib.fa_bwd_workspace_bytes.restype = Z
     lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, Z, P]
@@ -292,13 +295,18 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, max_seqlen_
                                 int(bool(causal)), _stream(stream)), "fa_fwd_varlen")
 
 
-def fa_fp8_quantize(x, signs, codes, scales, B, H, N, d, stream=None):
-    """bf16 [B,H,N,d] -> E4M3FN codes + fp32 [B,H,ceil(N/64)] scales; signs [d] rotates."""
-    _check(load().fa_fp8_quantize(_ptr(x, 2 * _n(B, H, N, d), "x", BF16),
-                                  _ptr(signs, 4 * _n(d), "signs", F32),
-                                  _ptr(codes, _n(B, H, N, d), "codes", U8),
-                                  _ptr(scales, 4 * _n(B, H, (int(N) + 63) // 64), "scales", F32),
-                                  B, H, N, d, _stream(stream)), "fa_fp8_quantize")
+def fa_fp8_quantize(x, signs, codes, scales, B, H, N, d, stream=None, scale_rule=None):
+    """bf16 [B,H,N,d] -> E4M3FN codes + fp32 [B,H,ceil(N/64)] scales; signs [d] rotates.
+    ``scale_rule`` FA_FP8_SCALE_AMAX (max|x| / 448, the default) or
+    FA_FP8_SCALE_POW2 (the smallest power of two with max|x| / scale <= 448)."""
+    args = (_ptr(x, 2 * _n(B, H, N, d), "x", BF16), _ptr(signs, 4 * _n(d), "signs", F32),
+            _ptr(codes, _n(B, H, N, d), "codes", U8),
+            _ptr(scales, 4 * _n(B, H, (int(N) + 63) // 64), "scales", F32), B, H, N, d)
+    if scale_rule is None:
+        _check(load().fa_fp8_quantize(*args, _stream(stream)), "fa_fp8_quantize")
+    else:
+        _check(load().fa_fp8_quantize_ex(*args, int(scale_rule), _stream(stream)),
+               "fa_fp8_quantize_ex")
 
 
 def fa_decode_splitkv_varlen(q, kcache, vcache, o, lse, seqlens_k, B, Hq, Hkv, Lkv, d, num_splits,

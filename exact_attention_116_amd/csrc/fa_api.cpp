@@ -350,6 +350,13 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
 
 fa_status fa_fp8_quantize(const void* x, const float* signs, void* codes, float* scales, int B,
                           int H, int N, int d, void* stream) {
+  return fa_fp8_quantize_ex(x, signs, codes, scales, B, H, N, d, FA_FP8_SCALE_AMAX, stream);
+}
+
+fa_status fa_fp8_quantize_ex(const void* x, const float* signs, void* codes, float* scales,
+                             int B, int H, int N, int d, int scale_rule, void* stream) {
+  if (scale_rule != FA_FP8_SCALE_AMAX && scale_rule != FA_FP8_SCALE_POW2)
+    return fail(FA_ERR_INVALID_ARG, "scale_rule must be FA_FP8_SCALE_AMAX or FA_FP8_SCALE_POW2");
   if (!aligned16(x) || !aligned16(codes) || !scales || (reinterpret_cast<uintptr_t>(scales) & 3u))
     return fail(FA_ERR_INVALID_ARG,
                 "x and codes must be non-NULL and 16-byte aligned, scales non-NULL and 4-byte aligned");
@@ -363,6 +370,7 @@ fa_status fa_fp8_quantize(const void* x, const float* signs, void* codes, float*
   fa::QuantArgs a{};
   a.x = x; a.signs = signs; a.codes = codes; a.scales = scales;
   a.B = B; a.H = H; a.N = N; a.d = d;
+  a.pow2 = scale_rule == FA_FP8_SCALE_POW2;
   a.stream = stream;
   hipError_t e = fa::launch_fp8_quant(a);
   if (e != hipSuccess) return hip_fail(e, "fa_fp8_quantize launch");

@@ -4,8 +4,9 @@
 // Method: the FlashAttention-3 snippets pair block quantisation with
 // "incoherent processing" to cut fp8 error.  Block quantisation here is the
 // fp8 forward pass's input format: per (batch, head) and 64-row block,
-// scale = max|x| / 448 (1 for an all-zero block) and code = E4M3FN(x /
-// scale), nearest with ties to even.  Incoherent processing is read as the
+// scale = max|x| / 448, or the smallest power of two with max|x| / scale <=
+// 448 (1 for an all-zero block either way), and code = E4M3FN(x / scale),
+// nearest with ties to even.  Incoherent processing is read as the
 // multiplication of each row by diag(s) H_d / sqrt(d) -- random signs s, the
 // Sylvester-ordered Walsh-Hadamard matrix H_d -- before the scale is taken;
 // applied to Q and K with the same s it leaves Q K^T unchanged while
@@ -33,8 +34,9 @@
 //  * Plain blocks quantise the fragments as read: eight consecutive columns
 //    of one row per 16-column step.
 // The 1/sqrt(d) factor is folded into the block's reciprocal scale, and each
-// ratio x * (448 / max|x|) (within an ulp or so of x / scale) is clamped to
-// +-448 and converted by v_cvt_pk_fp8_f32 (nearest, ties to even).  The
+// ratio x * (448 / max|x|) (within an ulp or so of x / scale), or x * 2^-k
+// for a power-of-two scale 2^k (exact), is clamped to +-448 and converted by
+// v_cvt_pk_fp8_f32 (nearest, ties to even).  The
 // codes go back through LDS, four to a 32-bit word, so that every store
 // instruction writes 1 KB of consecutive rows.
 #include "fa_device.hpp"
@@ -47,7 +49,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(128, 128)))
 __attribute__((amdgpu_waves_per_eu(3)))
 void fa_fp8_quant_kernel(const bf16* __restrict__ x, const float* __restrict__ signs,
                              uint8_t* __restrict__ codes, float* __restrict__ scales, int N,
-                             int rtiles) {
+                             int rtiles, int pow2) {
   constexpr int RB = D * 2;             // bytes per bf16 row
   constexpr int NCH = RB / 16;          // 16-byte chunks per row
   constexpr int ROWS = 64;              // one scale block, 32 rows per wave
@@ -154,8 +156,16 @@ void fa_fp8_quant_kernel(const bf16* __restrict__ x, const float* __restrict__ s
   if (lane == 0) wmax[wave] = amax;
   __syncthreads();                      // wmax is set and every X fragment has been read
   amax = fmaxf(wmax[0], wmax[1]) * fct;
-  const float scale = amax > 0.f ? amax / 448.f : 1.f;
-  const float rinv = amax > 0.f ? fct * (448.f / amax) : 0.f;
+  float scale = amax > 0.f ? amax / 448.f : 1.f;
+  float rinv = amax > 0.f ? fct * (448.f / amax) : 0.f;
+  if (pow2 && amax > 0.f) {
+    // amax = f 2^e, f in [0.5, 1), 448 = 0.875 2^9: the smallest 2^k with
+    // amax <= 448 2^k has k = e - 9 for f <= 0.875, else e - 8
+    const int e = __builtin_amdgcn_frexp_expf(amax);
+    const int kk = __builtin_amdgcn_frexp_mantf(amax) <= 0.875f ? e - 9 : e - 8;
+    scale = __builtin_amdgcn_ldexpf(1.f, kk);
+    rinv = __builtin_amdgcn_ldexpf(fct, -kk);
+  }
   if (tid == 0) scales[(size_t)bh * ((N + 63) >> 6) + rt] = scale;
 
   // codes: four consecutive columns of row r per 32-bit word, into LDS with
@@ -196,10 +206,10 @@ static hipError_t launch_quant_d(const QuantArgs& a) {
   hipStream_t st = (hipStream_t)a.stream;
   if (a.signs)
     hipLaunchKernelGGL((fa_fp8_quant_kernel<D, true>), dim3((unsigned)grid), dim3(128), 0, st,
-                       (const bf16*)a.x, a.signs, (uint8_t*)a.codes, a.scales, a.N, rtiles);
+                       (const bf16*)a.x, a.signs, (uint8_t*)a.codes, a.scales, a.N, rtiles, a.pow2);
   else
     hipLaunchKernelGGL((fa_fp8_quant_kernel<D, false>), dim3((unsigned)grid), dim3(128), 0, st,
-                       (const bf16*)a.x, a.signs, (uint8_t*)a.codes, a.scales, a.N, rtiles);
+                       (const bf16*)a.x, a.signs, (uint8_t*)a.codes, a.scales, a.N, rtiles, a.pow2);
   return hipGetLastError();
 }
 

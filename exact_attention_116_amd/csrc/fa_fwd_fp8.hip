@@ -27,7 +27,10 @@
 //    product covers exactly one 64-key V block), and the accumulator is kept
 //    in units of the current block's r_t: before the products of block t it
 //    is multiplied by r_{t-1} / r_t (merged with the running-max rescale).
-//    The epilogue multiplies by r_last * 2^e_max once.
+//    The epilogue multiplies by r_last * 2^e_max once.  When every V scale
+//    of the head has the same mantissa (power-of-two scales, say), all the
+//    ratios are 1 and the loop runs in a second form without those
+//    multiplies: one multiply per accumulator element and 64 keys fewer.
 //  * The running max is moved only when it would grow by more than 0.75 (base
 //    2), so every weight times 256 stays below 256 * 2^0.75 < 448, the
 //    largest E4M3FN value; skipped rescales leave the result exact.
@@ -40,6 +43,7 @@
 namespace fa {
 
 namespace {
+template <bool B> struct BoolC { static constexpr bool value = B; };
 constexpr int D = 128;
 constexpr float kLog2PScale = 8.f;  // P is rounded as 256 * p
 constexpr float kLazy = 0.75f;      // 256 * 2^0.75 = 430.5 < 448
@@ -64,9 +68,11 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
-// Pack four floats to E4M3FN bytes (x0 in the lowest byte).
+// Pack four floats to E4M3FN bytes (x0 in the lowest byte).  The first
+// conversion's other half is overwritten by the second, so it starts from
+// x0's own bits rather than a zeroed register (no v_mov per word).
 __device__ __forceinline__ uint32_t pack_fp8x4(float x0, float x1, float x2, float x3) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, __builtin_bit_cast(int, x0), false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
   return (uint32_t)w;
 }
@@ -126,6 +132,11 @@ void fa_fwd_fp8_dl_kernel(const uint8_t* __restrict__ q, const uint8_t* __restri
   for (int i = lane; i < nsb; i += 64) svmax = fmaxf(svmax, vsh[i]);
   svmax = wave_max(svmax);
   const int e_max = __builtin_amdgcn_frexp_expf(svmax);
+  // do all V scales of the head share one mantissa?
+  const float r_first = __builtin_amdgcn_frexp_mantf(vsh[0]);
+  bool rdiff = false;
+  for (int i = lane; i < nsb; i += 64) rdiff |= __builtin_amdgcn_frexp_mantf(vsh[i]) != r_first;
+  const bool one_mantissa = __builtin_amdgcn_ballot_w64(rdiff) == 0;
 
   const int q0 = qt * BRW;
   const int qw = q0 + wave * 32;
@@ -208,6 +219,9 @@ void fa_fwd_fp8_dl_kernel(const uint8_t* __restrict__ q, const uint8_t* __restri
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
 
+  // the key loop; MULV: V's block mantissas differ, so acc changes units
+  auto key_loop = [&](auto mulv) __attribute__((always_inline)) {
+  constexpr bool MULV = decltype(mulv)::value;
   for (int j = 0; j < ntiles; ++j) {
     const bool more = j + 1 < ntiles;
     if (more) load_tile(j + 1);
@@ -283,6 +297,12 @@ void fa_fwd_fp8_dl_kernel(const uint8_t* __restrict__ q, const uint8_t* __restri
         alpha = (m_cand == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m - m_cand);
         m = m_cand;
         l *= alpha;
+        if constexpr (!MULV) {
+#pragma unroll
+          for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[cb][i] *= alpha;
+        }
       }
       const float mref = (m == kNegInf) ? 0.f : m;
       const float bias = kLog2PScale - mref;
@@ -296,20 +316,24 @@ void fa_fwd_fp8_dl_kernel(const uint8_t* __restrict__ q, const uint8_t* __restri
       for (int hh = 0; hh < 2; ++hh) {
         if (hh == 0 || h1) {
           const float sv = vsh[sb0 + hh];
-          const float rt = __builtin_amdgcn_frexp_mantf(sv);
           sa[hh] = max(kE8M0One + __builtin_amdgcn_frexp_expf(sv) - e_max, 0);
-          fac[hh] = r_cur * __builtin_amdgcn_rcpf(rt);
-          r_cur = rt;
+          if constexpr (MULV) {
+            const float rt = __builtin_amdgcn_frexp_mantf(sv);
+            fac[hh] = r_cur * __builtin_amdgcn_rcpf(rt);
+            r_cur = rt;
+          }
         } else {
           sa[hh] = kE8M0One;
           fac[hh] = 1.f;
         }
       }
-      fac[0] *= alpha;
+      if constexpr (MULV) {
+        fac[0] *= alpha;
 #pragma unroll
-      for (int cb = 0; cb < D / 32; ++cb)
+        for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[cb][i] *= fac[0];
+          for (int i = 0; i < 16; ++i) acc[cb][i] *= fac[0];
+      }
 
       i32x8 pb[2];
 #pragma unroll
@@ -354,7 +378,8 @@ void fa_fwd_fp8_dl_kernel(const uint8_t* __restrict__ q, const uint8_t* __restri
           if (i >= PD) {
             const int x = i - PD, hh = x / (D / 32), cb = x % (D / 32);
             // the second block's products start from acc in its units
-            acc[cb] = mfma32x32x64_fp8_sa(vf[x], pb[hh], hh == 0 ? acc[cb] : acc[cb] * fac[1], sa[hh]);
+            acc[cb] = mfma32x32x64_fp8_sa(vf[x], pb[hh], (hh == 0 || !MULV) ? acc[cb] : acc[cb] * fac[1],
+                                          sa[hh]);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -364,6 +389,11 @@ void fa_fwd_fp8_dl_kernel(const uint8_t* __restrict__ q, const uint8_t* __restri
     if (more) __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
+  };
+  if (one_mantissa)
+    key_loop(BoolC<false>{});
+  else
+    key_loop(BoolC<true>{});
 
   l = sum_pair32(l);
   // acc holds 256 * sum_t (r_t / r_last) sum_j p_j code_j 2^(e_t - e_max)

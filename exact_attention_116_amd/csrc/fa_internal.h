@@ -80,6 +80,7 @@ struct QuantArgs {
   void* codes;          // u8 [B, H, N, d]
   float* scales;        // [B, H, ceil(N/64)]
   int B, H, N, d;
+  int pow2;             // power-of-two scales (else max|x| / 448)
   void* stream;
 };
 

@@ -281,6 +281,28 @@ fa_status fa_fp8_quantize(const void* x, const float* signs, void* codes, float*
                           int H, int N, int d, void* stream);
 
 /*
+ * fa_fp8_quantize_ex -- fa_fp8_quantize with a choice of the block scale.
+ * FA_FP8_SCALE_AMAX is fa_fp8_quantize's max|x| / 448.  FA_FP8_SCALE_POW2
+ * takes the smallest power of two with max|x| / scale <= 448 (1 for an
+ * all-zero block): the E8M0 form of the matrix cores' operand scale.  For
+ * V this is the fast form: the fp8 forward pass applies a power of two to
+ * V's products inside the MFMA, and when all of a head's V scales share one
+ * mantissa it needs no per-block multiply of its accumulator.  Q and K are
+ * better kept at max|x| / 448, which makes each block's largest element
+ * exact (their scales cost nothing in the forward pass).  With the POW2 rule
+ * and no rotation, x / scale is exact and the codes are the nearest-even
+ * E4M3FN values of it.  Other scale_rule values: FA_ERR_INVALID_ARG.  The
+ * rest as fa_fp8_quantize.
+ */
+typedef enum {
+  FA_FP8_SCALE_AMAX = 0,
+  FA_FP8_SCALE_POW2 = 1
+} fa_fp8_scale_rule;
+
+fa_status fa_fp8_quantize_ex(const void* x, const float* signs, void* codes, float* scales,
+                             int B, int H, int N, int d, int scale_rule, void* stream);
+
+/*
  * fa_bwd -- gradients of exact attention: dQ, dK, dV for an upstream dO,
  * with P recomputed from Q, K and the forward pass's LSE (the recomputation
  * of the FlashAttention summaries; the FlashAttention-2 overview, section

@@ -231,6 +231,21 @@ def test_fp8_quantize_rejects(lib, kw, status):
 
 
 @pytest.mark.parametrize("kw,status", [
+    (dict(rule=2), fa.FA_ERR_INVALID_ARG),
+    (dict(rule=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(rule=fa.FA_FP8_SCALE_POW2, x=None), fa.FA_ERR_INVALID_ARG),
+    (dict(rule=fa.FA_FP8_SCALE_POW2, d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(rule=fa.FA_FP8_SCALE_AMAX, B=0), fa.FA_ERR_INVALID_ARG),
+])
+def test_fp8_quantize_ex_rejects(lib, kw, status):
+    a = dict(x=A, signs=None, codes=A, scales=A, B=1, H=2, N=100, d=128, rule=0)
+    a.update(kw)
+    st = lib.fa_fp8_quantize_ex(a["x"], a["signs"], a["codes"], a["scales"], a["B"], a["H"],
+                                a["N"], a["d"], a["rule"], None)
+    assert st == status
+
+
+@pytest.mark.parametrize("kw,status", [
     (dict(seq=None), fa.FA_ERR_INVALID_ARG),
     (dict(seq=A + 2), fa.FA_ERR_INVALID_ARG),
     (dict(Hkv=3), fa.FA_ERR_INVALID_ARG),

@@ -64,10 +64,14 @@ def check_head(og, lg, q, k, v, scale, causal, rows, what, model=False):
     return err, err_model
 
 
-def gen(wid, B, H, N, d, outlier_p=1e-3):
+def gen(wid, B, H, N, d, outlier_p=1e-3, v_pow2=True):
+    """Q and K with max|x| / 448 block scales; V with power-of-two scales
+    (the workload's rule), or with ``v_pow2=False`` max|x| / 448 too, whose
+    mantissas differ from block to block."""
     codes, scales = [], []
     for t in (fi.Q_ID, fi.K_ID, fi.V_ID):
-        c, s = fi.fp8_tensor(wid, t, B, H, N, d, outlier_p=outlier_p)
+        c, s = fi.fp8_tensor(wid, t, B, H, N, d, outlier_p=outlier_p,
+                             pow2=v_pow2 if t == fi.V_ID else False)
         codes.append(c)
         scales.append(s)
     return codes, scales
@@ -92,14 +96,17 @@ def test_fp8_code_semantics(gpu_lib):
     assert np.array_equal(og, ref), (og[0, 0, 0, :8], ref[0, 0, 0, :8])
 
 
+@pytest.mark.parametrize("v_pow2", [True, False])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 2, 33, 64, 65, 127, 128, 200, 257, 640])
-def test_fp8_edge_shapes(gpu_lib, N, causal):
+def test_fp8_edge_shapes(gpu_lib, N, causal, v_pow2):
+    """V scales of one mantissa per head (powers of two) run the loop form
+    without per-block multiplies, max|x| / 448 scales the other form."""
     fa = gpu_lib
     B, H, d = 2, 3, 128
     wid = 5000 + 4 * N + causal
-    say(f"fp8 edge B={B} H={H} N={N} causal={causal} seed-id={wid}")
-    codes, scales = gen(wid, B, H, N, d, outlier_p=1e-2)
+    say(f"fp8 edge B={B} H={H} N={N} causal={causal} v_pow2={v_pow2} seed-id={wid}")
+    codes, scales = gen(wid, B, H, N, d, outlier_p=1e-2, v_pow2=v_pow2)
     og, lg = run_fp8(fa, codes, scales, B, H, N, d, d ** -0.5, causal)
     deq = [oracle.dequant_fp8_rows(c, s) for c, s in zip(codes, scales)]
     errs, errs_model = [], []
@@ -124,13 +131,15 @@ def full_size_rows(N, tile, seed, n_random=512):
     return np.unique(np.r_[edges, rnd])
 
 
-def test_fp8_full_size(gpu_lib):
+@pytest.mark.parametrize("v_pow2", [True, False])
+def test_fp8_full_size(gpu_lib, v_pow2):
     """B=4, H=16, N=8192, d=128, causal, 0.1% x20 outliers: every (b, h) on
-    the tile-edge rows and 512 random rows each."""
+    the tile-edge rows and 512 random rows each; V with power-of-two block
+    scales (the workload) and with max|x| / 448 scales."""
     fa = gpu_lib
     w = fi.WORKLOADS[5]
-    say(f"fp8 {w.name}: generating")
-    codes, scales = gen(w.wid, w.B, w.H, w.N, w.d)
+    say(f"fp8 {w.name} v_pow2={v_pow2}: generating")
+    codes, scales = gen(w.wid, w.B, w.H, w.N, w.d, v_pow2=v_pow2)
     say("fp8 full size: running")
     og, lg = run_fp8(fa, codes, scales, w.B, w.H, w.N, w.d, w.scale, True)
     assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg))
@@ -149,6 +158,30 @@ def test_fp8_full_size(gpu_lib):
     say(f"  mean-abs over all heads' checked rows: {mean:.3e} (F3 gate {F3_MEAN_ABS}); "
         f"P-rounding model on heads h=0,8: {mean_model:.3e}")
     assert mean <= F3_MEAN_ABS, (mean, mean_model)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_v_scale_mantissas(gpu_lib, causal):
+    """Per head, V scales that share a mantissa other than 1/2 (3/4 here),
+    and heads where one block's mantissa differs from the rest: both loop
+    forms against the oracle on the same codes, N = 700 (11 scale blocks,
+    a ragged tail)."""
+    fa = gpu_lib
+    B, H, N, d = 1, 4, 700, 128
+    wid = 5950 + causal
+    say(f"fp8 V-scale mantissas B={B} H={H} N={N} causal={causal} seed-id={wid}")
+    codes, scales = gen(wid, B, H, N, d, outlier_p=1e-2)
+    vs = scales[2].copy()
+    vs[0, 0] *= np.float32(0.75)                 # one mantissa, 3/4
+    vs[0, 1, 5] *= np.float32(0.75)              # one block differs
+    vs[0, 2, -1] *= np.float32(1.5)              # the ragged last block differs
+    # head 3 keeps its power-of-two scales
+    scales = [scales[0], scales[1], vs]
+    og, lg = run_fp8(fa, codes, scales, B, H, N, d, d ** -0.5, causal)
+    deq = [oracle.dequant_fp8_rows(c, s) for c, s in zip(codes, scales)]
+    for h in range(H):
+        check_head(og[0, h], lg[0, h], deq[0][0, h], deq[1][0, h], deq[2][0, h], d ** -0.5,
+                   causal, np.arange(N), f"h={h}")
 
 
 def test_fp8_deterministic_and_in_bounds(gpu_lib):

@@ -21,12 +21,12 @@ from test_gpu_fp8 import check_head
 pytestmark = pytest.mark.gpu
 
 
-def quantize(fa, xb, B, H, N, d, signs=None):
+def quantize(fa, xb, B, H, N, d, signs=None, rule=None):
     x = bf16_to_dev(xb)
     codes = torch.empty((B, H, N, d), dtype=torch.uint8, device="cuda")
     scales = torch.empty((B, H, (N + 63) // 64), dtype=torch.float32, device="cuda")
     sg = None if signs is None else torch.from_numpy(signs).cuda()
-    fa.fa_fp8_quantize(x, sg, codes, scales, B, H, N, d)
+    fa.fa_fp8_quantize(x, sg, codes, scales, B, H, N, d, scale_rule=rule)
     torch.cuda.synchronize()
     return codes, scales
 
@@ -69,6 +69,40 @@ def test_quantize_codes_and_scales(gpu_lib, N, rot, d):
     check_codes(codes, scales, oracle.decode_bf16(xb), signs, f"N={N} d={d} rot={rot}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("rot", [False, True])
+@pytest.mark.parametrize("N", [1, 64, 65, 300, 1000])
+def test_quantize_pow2_scales(gpu_lib, N, rot, d):
+    """The power-of-two scale rule: scales equal the oracle's (the smallest
+    2^k with max|x| / 2^k <= 448); without rotation x / scale is exact, so
+    every code equals the oracle's nearest-even code; with rotation the
+    ratio carries the rotation's fp32 rounding and near-midpoints may take
+    either neighbour, as for the max|x| / 448 rule."""
+    fa = gpu_lib
+    B, H = 2, 3
+    wid = 9150 + 3 * N + 2 * rot + (d == 128)
+    say(f"fp8 quantise, power-of-two scales B={B} H={H} N={N} d={d} rotate={rot} seed-id={wid}")
+    xb = fi.outlier_bf16_tensor(wid, fi.V_ID, B, H, N, d)
+    signs = fi.rotation_signs(wid, d) if rot else None
+    codes, scales = quantize(fa, xb, B, H, N, d, signs, rule=fa.FA_FP8_SCALE_POW2)
+    x64 = oracle.decode_bf16(xb)
+    y = x64 if signs is None else oracle.incoherent_rotation(x64, signs)
+    _, s_ref, ratio = oracle.quantize_e4m3_blocks(y, pow2=True)
+    sg = scales.cpu().numpy().astype(np.float64)
+    np.testing.assert_array_equal(sg, s_ref)
+    got = oracle.decode_e4m3fn(codes.cpu().numpy())
+    want = oracle.round_to_e4m3fn(ratio)
+    if not rot:
+        np.testing.assert_array_equal(got, want)
+        say(f"  every code equal")
+    else:
+        diff = got != want
+        a = np.abs(ratio[diff])
+        mid = (np.abs(got[diff]) + np.abs(want[diff])) / 2
+        say(f"  {diff.sum()} of {diff.size} codes at near-midpoints")
+        assert np.all(np.abs(a - mid) <= 1e-5 * a) and np.mean(diff) < 1e-2
+
+
 def test_quantize_zero_block(gpu_lib):
     fa = gpu_lib
     B, H, N, d = 1, 1, 130, 128
@@ -96,8 +130,9 @@ def test_rotated_fp8_forward(gpu_lib):
     errs = {}
     for rot in (False, True):
         sg = signs if rot else None
-        (qc, qs), (kc, ks), (vc, vs) = (quantize(fa, x, B, H, N, d, s) for x, s in
-                                        ((xs[0], sg), (xs[1], sg), (xs[2], None)))
+        (qc, qs), (kc, ks), (vc, vs) = (quantize(fa, x, B, H, N, d, s, r) for x, s, r in
+                                        ((xs[0], sg, None), (xs[1], sg, None),
+                                         (xs[2], None, fa.FA_FP8_SCALE_POW2)))
         o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
         lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
         fa.fa_fwd_ex(qc, kc, vc, o, lse, B, H, N, d, scale, True, in_dtype=fa.FA_FP8_E4M3,
