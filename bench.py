@@ -397,7 +397,7 @@ def main():
                 raise
             return False
 
-    if want("c5") and fp8_built():
+    if (want("c5") or want("c5a")) and fp8_built():
         if True:
             x = {}
             for n, t in (("q", 0), ("k", 1), ("v", 2)):
@@ -414,20 +414,21 @@ def main():
             run5()
             torch.cuda.synchronize()
             n5 = w5.B * w5.H * w5.N
-            jobs.append(("c5", run5, fwd_flops(w5, True),
-                         3 * n5 * w5.d + 3 * n5 // 64 * 4 + n5 * w5.d * 2 + n5 * 4, "fwd_fp8"))
-            # the same codes of Q and K, V quantised with max|x| / 448 scales,
-            # whose mantissas differ between blocks
-            c, s = fi.fp8_tensor(w5.wid, fi.V_ID, w5.B, w5.H, w5.N, w5.d, pow2=False)
-            x["va"] = torch.from_numpy(c).to(dev)
-            x["vas"] = torch.from_numpy(s).to(dev)
+            bytes5 = 3 * n5 * w5.d + 3 * n5 // 64 * 4 + n5 * w5.d * 2 + n5 * 4
+            if want("c5"):
+                jobs.append(("c5", run5, fwd_flops(w5, True), bytes5, "fwd_fp8"))
+            if want("c5a"):
+                # the same codes of Q and K, V quantised with max|x| / 448
+                # scales, whose mantissas differ between blocks
+                c, s = fi.fp8_tensor(w5.wid, fi.V_ID, w5.B, w5.H, w5.N, w5.d, pow2=False)
+                x["va"] = torch.from_numpy(c).to(dev)
+                x["vas"] = torch.from_numpy(s).to(dev)
 
-            def run5a():
-                fa.fa_fwd_ex(x["q"], x["k"], x["va"], o5, l5, w5.B, w5.H, w5.N, w5.d, w5.scale,
-                             True, in_dtype=fa.FA_FP8_E4M3, q_scale=x["qs"], k_scale=x["ks"],
-                             v_scale=x["vas"], stream=stream)
-            jobs.append(("c5a", run5a, fwd_flops(w5, True),
-                         3 * n5 * w5.d + 3 * n5 // 64 * 4 + n5 * w5.d * 2 + n5 * 4, "fwd_fp8"))
+                def run5a():
+                    fa.fa_fwd_ex(x["q"], x["k"], x["va"], o5, l5, w5.B, w5.H, w5.N, w5.d,
+                                 w5.scale, True, in_dtype=fa.FA_FP8_E4M3, q_scale=x["qs"],
+                                 k_scale=x["ks"], v_scale=x["vas"], stream=stream)
+                jobs.append(("c5a", run5a, fwd_flops(w5, True), bytes5, "fwd_fp8"))
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
