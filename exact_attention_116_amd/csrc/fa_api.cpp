@@ -378,9 +378,14 @@ fa_status fa_fp8_quantize_ex(const void* x, const float* signs, void* codes, flo
   return FA_OK;
 }
 
+// Two fp32 row arrays, -D and -LSE/scale, the second starting 256-byte
+// aligned after the first.
+static size_t bwd_rows_padded(size_t rows) { return (rows + 63u) & ~(size_t)63u; }
+
 size_t fa_bwd_workspace_bytes(int B, int H, int N) {
   if (B < 1 || H < 1 || N < 1) return 0;
-  const size_t n = (size_t)B * H * (size_t)N * 4u;
+  const size_t rows = (size_t)B * H * (size_t)N;
+  const size_t n = (bwd_rows_padded(rows) + rows) * 4u;
   return (n + 255u) & ~(size_t)255u;
 }
 
@@ -415,7 +420,8 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
   }
   fa::BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
-  a.dsum = static_cast<float*>(ws);
+  a.ndsum = static_cast<float*>(ws);
+  a.nlse = a.ndsum + bwd_rows_padded((size_t)B * H * (size_t)N);
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.B = B; a.H = H; a.N = N; a.d = d;
   a.scale = scale;
@@ -478,7 +484,8 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
   }
   fa::BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
-  a.dsum = static_cast<float*>(ws);
+  a.ndsum = static_cast<float*>(ws);
+  a.nlse = a.ndsum + bwd_rows_padded((size_t)H * total_q);
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.B = B; a.H = H; a.N = max_seqlen_q; a.d = d;
   a.scale = scale;

@@ -17,7 +17,8 @@
 // roundings of P and dS; the statistics stay fp32.
 //
 // Packed batches of unequal lengths (PACKED instances) use the same kernels
-// with runtime row strides: [total, H, d] rows, LSE and D as [H, total_q],
+// with runtime row strides: [total, H, d] rows, LSE and the row arrays of
+// the workspace as [H, total_q],
 // each workgroup's sequence found from the cumulative lengths, and causal
 // masking aligned at the sequence end (query i sees key j iff
 // j <= i + Lk - Lq).  A query that sees no key gets dQ = 0; keys of a
@@ -25,7 +26,8 @@
 //
 // Three kernels, none of which needs atomics (so the result is
 // deterministic):
-//  1. fa_bwd_pre_kernel: D per query row, fp32, from bf16 O and dO.
+//  1. fa_bwd_pre_kernel: per query row, -D (fp32, from bf16 O and dO) and
+//     -LSE/scale, the starting values of the dK/dV kernel's accumulators.
 //  2. fa_bwd_dkdv_kernel: key/value tiles outer, query tiles inner.  A pair
 //     of waves owns 32 keys; K^T (one wave) and V^T (the other) stay in
 //     VGPRs as MFMA B operands.  Per 32-query block one wave forms
@@ -175,15 +177,20 @@ __device__ __forceinline__ BwdSeq bwd_seq(const BwdLayout& lay, int bh) {
 }
 
 // ---------------------------------------------------------------------------
-// 1. D = rowsum(dO * O)
+// 1. -D = -rowsum(dO * O), and -LSE/scale
 // ---------------------------------------------------------------------------
 // Rows are contiguous d-element rows of O and dO.  Dense: row r is (b*H+h)*N
-// + n and D goes to dsum[r].  Packed (H > 0): row r is token r/H, head r%H,
-// and D goes to dsum[(r%H) * total_q + r/H] ([H, total_q], the LSE layout).
+// + n and its values go to index r.  Packed (H > 0): row r is token r/H, head
+// r%H, at index (r%H) * total_q + r/H ([H, total_q], the LSE layout).  Both
+// values are the starting values of the dK/dV kernel's accumulators, stored
+// so that its loop takes them as loaded (16 VALU operations fewer per
+// 32-query block and wave).
 template <int D, bool F16>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void fa_bwd_pre_kernel(const bf16* __restrict__ o, const bf16* __restrict__ dout,
-                       float* __restrict__ dsum, long long rows, int H, int total_q) {
+                       const float* __restrict__ lse, float* __restrict__ ndsum,
+                       float* __restrict__ nlse, long long rows, int H, int total_q,
+                       float neg_inv_scale) {
   constexpr int LPR = D / 8;  // lanes per row, 16 bytes each
   const long long row = (long long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
   const int part = threadIdx.x % LPR;
@@ -197,7 +204,8 @@ void fa_bwd_pre_kernel(const bf16* __restrict__ o, const bf16* __restrict__ dout
   acc = group_sum<LPR>(acc);
   if (row < rows && part == 0) {
     const long long at = H > 0 ? (long long)(row % H) * total_q + row / H : row;
-    dsum[at] = acc;
+    ndsum[at] = -acc;
+    nlse[at] = lse[at] * neg_inv_scale;
   }
 }
 
@@ -230,14 +238,14 @@ __device__ __forceinline__ void lds_barrier() {
 // for block b - 1 runs on the matrix cores, and role 1 forms dP of block b
 // while it computes dS of block b - 1, then adds block b - 1 into dK^T.
 // LSE and D enter as the starting values of the S and dP accumulators
-// (-LSE/scale and -D), so P = exp2(c s) and dS = P s without a per-element
-// correction.  Q and dO rows are read row-wise for the first product and
+// (-LSE/scale and -D, from the workspace as the first kernel stored them),
+// so P = exp2(c s) and dS = P s without a per-element correction.  Q and dO rows are read row-wise for the first product and
 // through ds_read_b64_tr_b16 for the second.
 template <int D, int BQ, bool CAUSAL, bool F16, bool PACKED, int PD = 3>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512)))
 void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                              const bf16* __restrict__ v, const bf16* __restrict__ dout,
-                             const float* __restrict__ lse, const float* __restrict__ dsum,
+                             const float* __restrict__ nlse, const float* __restrict__ ndsum,
                              bf16* __restrict__ dk, bf16* __restrict__ dv, int BH, BwdLayout lay,
                              float c /* scale*log2(e) */, float scale) {
   constexpr int NW = 8, NP = NW / 2;
@@ -268,13 +276,12 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int off = CAUSAL ? Lk - Lq : 0; // causal: query i sees keys j <= i + off
   const int kw = k0 + pair * 32;        // the pair's first key
   const int my_key = kw + l32;
-  const float neg_inv_scale = -1.f / scale;
 
   const uint32_t RG = (uint32_t)rs * 2u;       // bytes from one row to the next in memory
   const rsrc_t Qr = make_rsrc(q + sq.qbase, (uint32_t)Lq * RG);
   const rsrc_t Or = make_rsrc(dout + sq.qbase, (uint32_t)Lq * RG);
-  const rsrc_t Lr = make_rsrc(lse + sq.lbase, (uint32_t)Lq * 4u);
-  const rsrc_t Dr = make_rsrc(dsum + sq.lbase, (uint32_t)Lq * 4u);
+  const rsrc_t Lr = make_rsrc(nlse + sq.lbase, (uint32_t)Lq * 4u);
+  const rsrc_t Dr = make_rsrc(ndsum + sq.lbase, (uint32_t)Lq * 4u);
 
   bf16x8 kv[D / 16];
   {
@@ -297,7 +304,7 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const uint32_t qoff = (uint32_t)it * BQ * RG;
     ld.load(Qr, qoff, st, wave);
     ld.load(Or, qoff, st + TILE, wave);
-    if (wave < 2 * (BQ / 64)) {           // LSE (even waves) and D (odd), 64 rows each
+    if (wave < 2 * (BQ / 64)) {           // -LSE/scale (even waves) and -D (odd), 64 rows each
       const int which = wave & 1, part = wave >> 1;
       const uint32_t off = ((uint32_t)it * BQ + 64 * part + lane) * 4u;
       lds_dma4(which ? Dr : Lr, st + 2 * TILE + which * BQ * 4 + 64 * part * 4, off);
@@ -376,7 +383,7 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           for (int gi = 0; gi < 4; ++gi) {
             const f32x4 x = *reinterpret_cast<const f32x4*>(Ls + 32 * blk + 8 * gi + 4 * g);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) s[4 * gi + j] = x[j] * neg_inv_scale;
+            for (int j = 0; j < 4; ++j) s[4 * gi + j] = x[j];
           }
           {
             bf16x8 f[NF1];
@@ -430,7 +437,7 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           for (int gi = 0; gi < 4; ++gi) {
             const f32x4 x = *reinterpret_cast<const f32x4*>(Ds + 32 * blk + 8 * gi + 4 * g);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) s[4 * gi + j] = -x[j];
+            for (int j = 0; j < 4; ++j) s[4 * gi + j] = x[j];
           }
           uint32_t sw[8];
           {
@@ -497,7 +504,7 @@ template <int D, int BC, int NW, bool CAUSAL, bool F16, bool PACKED>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                       const bf16* __restrict__ v, const bf16* __restrict__ dout,
-                      const float* __restrict__ lse, const float* __restrict__ dsum,
+                      const float* __restrict__ lse, const float* __restrict__ ndsum,
                       bf16* __restrict__ dq, int BH, BwdLayout lay, float c, float scale) {
   constexpr int RB = D * 2;
   constexpr int BR = NW * 32;           // queries per workgroup
@@ -527,9 +534,9 @@ void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const rsrc_t Kr = make_rsrc(k + sq.kbase, (uint32_t)Lk * RG);
   const rsrc_t Vr = make_rsrc(v + sq.kbase, (uint32_t)Lk * RG);
 
-  // Q^T and dO^T of this lane's query as B operands; its LSE (base 2) and D
+  // Q^T and dO^T of this lane's query as B operands; its LSE (base 2) and -D
   bf16x8 qb[D / 16], ob[D / 16];
-  float lse2 = 0.f, dd = 0.f;
+  float lse2 = 0.f, nd = 0.f;
   {
     const rsrc_t Qr = make_rsrc(q + sq.qbase, (uint32_t)Lq * RG);
     const rsrc_t Or = make_rsrc(dout + sq.qbase, (uint32_t)Lq * RG);
@@ -541,7 +548,7 @@ void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
     if (my_q < Lq) {
       lse2 = lse[sq.lbase + my_q] * kLog2e;
-      dd = dsum[sq.lbase + my_q];
+      nd = ndsum[sq.lbase + my_q];
     }
   }
 
@@ -613,7 +620,7 @@ void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
               const int key = kb0 + 8 * (i >> 2) + 4 * g + (i & 3);
               if (key >= Lk || my_q >= Lq || (CAUSAL && key > my_q + off)) p = 0.f;
             }
-            dsv[e] = p * (dp[i] - dd);
+            dsv[e] = p * (dp[i] + nd);
           }
           w[h] = pack16<F16>(dsv[0], dsv[1]);
         }
@@ -658,24 +665,25 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
   hipStream_t st = (hipStream_t)a.stream;
   const bool packed = PACKED;
   const BwdLayout lay{a.cu_q, a.cu_k, a.H, a.N, packed ? a.Nk : a.N, a.total_q, a.total_k};
-  // D for every query row: B*H*N dense rows, or total_q*H packed rows
+  // -D and -LSE/scale for every query row: B*H*N dense rows, or total_q*H
+  // packed rows
   const long long rows = packed ? (long long)a.total_q * a.H : (long long)BH * a.N;
   hipLaunchKernelGGL((fa_bwd_pre_kernel<D, F16>), dim3((unsigned)((rows + (256 / (D / 8)) - 1) / (256 / (D / 8)))),
-                     dim3(256), 0, st, (const bf16*)a.o, (const bf16*)a.dout, a.dsum, rows,
-                     packed ? a.H : 0, a.total_q);
+                     dim3(256), 0, st, (const bf16*)a.o, (const bf16*)a.dout, a.lse, a.ndsum, a.nlse,
+                     rows, packed ? a.H : 0, a.total_q, -1.f / a.scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nkt = (lay.Nk + BCK - 1) / BCK;   // of the longest key sequence
   hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BQ, CAUSAL, F16, PACKED>), dim3((unsigned)((long long)nkt * BH)),
                      dim3(NWK * 64), 0, st, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
-                     (const bf16*)a.dout, a.lse, a.dsum, (bf16*)a.dk, (bf16*)a.dv, BH, lay,
+                     (const bf16*)a.dout, a.nlse, a.ndsum, (bf16*)a.dk, (bf16*)a.dv, BH, lay,
                      a.scale_log2, a.scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nqt = (a.N + NWQ * 32 - 1) / (NWQ * 32);   // of the longest query sequence
   hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BCQ, NWQ, CAUSAL, F16, PACKED>), dim3((unsigned)((long long)nqt * BH)),
                      dim3(NWQ * 64), 0, st, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
-                     (const bf16*)a.dout, a.lse, a.dsum, (bf16*)a.dq, BH, lay, a.scale_log2,
+                     (const bf16*)a.dout, a.lse, a.ndsum, (bf16*)a.dq, BH, lay, a.scale_log2,
                      a.scale);
   return hipGetLastError();
 }

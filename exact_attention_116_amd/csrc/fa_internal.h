@@ -55,7 +55,8 @@ struct BwdArgs {
   const void* o;
   const void* dout;
   const float* lse;   // [B*H, N] natural log, from the forward pass
-  float* dsum;        // [B*H, N] workspace: rowsum(dO * O)
+  float* ndsum;       // [B*H, N] workspace: -rowsum(dO * O)
+  float* nlse;        // [B*H, N] workspace: -LSE / scale
   void* dq;
   void* dk;
   void* dv;
@@ -65,7 +66,8 @@ struct BwdArgs {
   int causal;
   int in_f16;         // fp16 tensors instead of bf16
   // packed sequences of unequal lengths (bf16): q, o, dout, dq are
-  // [total_q, H, d], k, v, dk, dv [total_k, H, d], lse and dsum [H, total_q];
+  // [total_q, H, d], k, v, dk, dv [total_k, H, d], lse, ndsum and nlse
+  // [H, total_q];
   // sequence b at rows cu_q[b].. and cu_k[b]..  N and Nk bound the query and
   // key lengths.  Null cu_q: the dense [B, H, N, d] layout.
   const int* cu_q;

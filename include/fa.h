@@ -317,9 +317,9 @@ fa_status fa_fp8_quantize_ex(const void* x, const float* signs, void* codes, flo
  * o and lse are the forward pass's outputs for the same q, k, v, scale and
  * causal flag (fa_fwd / fa_fwd_ex with bf16 output).  d in {64, 128}, else
  * FA_ERR_UNSUPPORTED; scale finite and > 0.  All pointers 16-byte aligned.
- * The workspace holds D (fp32 [B, H, N]): at least
- * fa_bwd_workspace_bytes(B, H, N) bytes, or NULL with workspace_bytes = 0 to
- * use the library-owned workspace (which allocates).  dq, dk and dv are
+ * The workspace holds -D and -LSE/scale (two fp32 [B, H, N] arrays): at
+ * least fa_bwd_workspace_bytes(B, H, N) bytes, or NULL with workspace_bytes
+ * = 0 to use the library-owned workspace (which allocates).  dq, dk and dv are
  * written in full (no accumulation into existing contents); the result is
  * deterministic (no atomics).
  */
@@ -361,8 +361,8 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
  *          query that sees no key gets dQ = 0; keys of a sequence without
  *          queries get dK = dV = 0.  Rows outside every sequence's range are
  *          not written.
- * The workspace holds D (fp32 [H, total_q]): at least
- * fa_bwd_workspace_bytes(1, H, total_q) bytes, or NULL with
+ * The workspace holds -D and -LSE/scale (two fp32 [H, total_q] arrays): at
+ * least fa_bwd_workspace_bytes(1, H, total_q) bytes, or NULL with
  * workspace_bytes = 0 for the library-owned workspace (which allocates).
  * d in {64, 128}, else FA_ERR_UNSUPPORTED; scale finite and > 0; pointers to
  * tensors 16-byte aligned, offsets 4-byte aligned.  One sequence's rows of

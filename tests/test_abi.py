@@ -290,7 +290,7 @@ def test_bwd_rejects(lib, kw, status):
     assert fa.fa_last_error() != ""
     if a["dtype"] == fa.FA_BF16:      # fa_bwd is fa_bwd_ex with FA_BF16
         assert lib.fa_bwd(*args, a["ws"], a["ws_bytes"], None) == status
-    assert fa.fa_bwd_workspace_bytes(1, 2, 100) == 1024   # 800 rounded up to 256
+    assert fa.fa_bwd_workspace_bytes(1, 2, 100) == 2048   # (256 + 200) * 4 rounded up to 256
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -319,7 +319,7 @@ def test_bwd_varlen_rejects(lib, kw, status):
     assert st == status
     assert fa.fa_last_error() != ""
     # D takes H * total_q fp32 values: the dense workspace of one batch of total_q rows
-    assert fa.fa_bwd_workspace_bytes(1, 4, 100) == 1792   # 1600 rounded up to 256
+    assert fa.fa_bwd_workspace_bytes(1, 4, 100) == 3584   # (448 + 400) * 4 rounded up to 256
 
 
 def test_binding_rejects_host_and_strided_tensors():
