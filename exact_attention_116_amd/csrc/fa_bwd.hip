@@ -394,10 +394,17 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
               __builtin_amdgcn_sched_barrier(0);
             }
           }
+          // masked scores to -inf, so that their weights come out as 0
+          if (edge) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int qi = qb0 + 8 * (e >> 2) + 4 * g + (e & 3);
+              if (qi >= Lq || (CAUSAL && my_key > qi + off)) s[e] = -__builtin_inff();
+            }
+          }
           // ---- P of this block, beside dV^T += dO^T P of the deferred block ----
           uint32_t pw[8];
-          auto mix = [&](auto EDGE) __attribute__((always_inline)) {
-            constexpr bool ED = decltype(EDGE)::value;
+          {
             bf16x8 f[NF2];
 #pragma unroll
             for (int i = 0; i < NS2; ++i) {
@@ -408,20 +415,13 @@ void fa_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
               }
               if (i < 8) {
                 const int e = 2 * i;
-                float p0 = __builtin_amdgcn_exp2f(s[e] * c);
-                float p1 = __builtin_amdgcn_exp2f(s[e + 1] * c);
-                if constexpr (ED) {
-                  const int qi = qb0 + 8 * (e >> 2) + 4 * g + (e & 3);
-                  if (qi >= Lq || (CAUSAL && my_key > qi + off)) p0 = 0.f;
-                  if (qi + 1 >= Lq || (CAUSAL && my_key > qi + 1 + off)) p1 = 0.f;
-                }
+                const float p0 = __builtin_amdgcn_exp2f(s[e] * c);
+                const float p1 = __builtin_amdgcn_exp2f(s[e + 1] * c);
                 pw[i] = pack16<F16>(p0, p1);
               }
               __builtin_amdgcn_sched_barrier(0);
             }
-          };
-          if (edge) mix(std::true_type{});
-          else mix(std::false_type{});
+          }
           *reinterpret_cast<u32x4*>(pb + 16 * lane) = u32x4{pw[0], pw[1], pw[2], pw[3]};
           *reinterpret_cast<u32x4*>(pb + 1024 + 16 * lane) = u32x4{pw[4], pw[5], pw[6], pw[7]};
           pbo[0] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
@@ -547,7 +547,10 @@ void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       ob[u] = __builtin_bit_cast(bf16x8, buf_load16(Or, o16));
     }
     if (my_q < Lq) {
-      lse2 = lse[sq.lbase + my_q] * kLog2e;
+      // a query that sees no key has LSE = -inf; +inf here makes every one of
+      // its weights exp2(-inf) = 0, masked or not
+      const float l = lse[sq.lbase + my_q];
+      lse2 = l > -__builtin_inff() ? l * kLog2e : __builtin_inff();
       nd = ndsum[sq.lbase + my_q];
     }
   }
@@ -605,6 +608,14 @@ void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       // (one comparison for both lengths: with separate ones the compiler's
       // register allocation of this loop spills)
       const bool edge = (CAUSAL && kb0 + 31 > qw + off) || max(kb0 + 32 - Lk, qw + 32 - Lq) > 0;
+      // masked scores to -inf, so that their weights come out as 0
+      if (edge) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb0 + 8 * (i >> 2) + 4 * g + (i & 3);
+          if (key >= Lk || my_q >= Lq || (CAUSAL && key > my_q + off)) s[i] = -__builtin_inff();
+        }
+      }
       bf16x8 ps[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -615,11 +626,7 @@ void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int i = 8 * t + 2 * h + e;
-            float p = __builtin_amdgcn_exp2f(fmaf(s[i], c, -lse2));
-            if (edge) {
-              const int key = kb0 + 8 * (i >> 2) + 4 * g + (i & 3);
-              if (key >= Lk || my_q >= Lq || (CAUSAL && key > my_q + off)) p = 0.f;
-            }
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c, -lse2));
             dsv[e] = p * (dp[i] + nd);
           }
           w[h] = pack16<F16>(dsv[0], dsv[1]);
