@@ -577,6 +577,12 @@ void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   wait_vm();
   __syncthreads();
 
+  // every dP^T block of this lane starts at its query's -D (16 registers
+  // held across the loop; the first MFMA of each chain reads them as C)
+  f32x16 ndv;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ndv[i] = nd;
+
   for (int j = 0; j < ntiles; ++j) {
     const bool more = j + 1 < ntiles;
     if (more) load_tile(j + 1);
@@ -589,7 +595,8 @@ void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       // the wave is past its sequence's queries, or the block lies above the diagonal
       if (qw >= Lq || (CAUSAL && kb0 > qw + 31 + off)) continue;
       // ---- S^T = K Q^T and dP^T = V dO^T: keys on rows, this lane's query on the column ----
-      f32x16 s = f32x16{}, dp = f32x16{};
+      // dP^T starts at -D (the lane's query), so dS = P dp
+      f32x16 s = f32x16{}, dp = ndv;
       {
         constexpr int PD = 4, NF = 2 * (D / 16);
         bf16x8 f[NF];
@@ -627,7 +634,7 @@ void fa_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           for (int e = 0; e < 2; ++e) {
             const int i = 8 * t + 2 * h + e;
             const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c, -lse2));
-            dsv[e] = p * (dp[i] + nd);
+            dsv[e] = p * dp[i];
           }
           w[h] = pack16<F16>(dsv[0], dsv[1]);
         }
