@@ -104,6 +104,11 @@ def test_varlen_and_quantize_and_backward_sizes():
                  Fake(B * H * 2, 4), B, H, N, d)
     raises_short("signs", fa.fa_fp8_quantize, Fake(B * H * N * d), Fake(d - 1, 4),
                  Fake(B * H * N * d, 1), Fake(B * H * 3, 4), B, H, N, d)
+    # the scale-rule form checks the same buffers
+    raises_short("scales", fa.fa_fp8_quantize, Fake(B * H * N * d), None, Fake(B * H * N * d, 1),
+                 Fake(B * H * 2, 4), B, H, N, d, scale_rule=fa.FA_FP8_SCALE_POW2)
+    raises_short("codes", fa.fa_fp8_quantize, Fake(B * H * N * d), None, Fake(B * H * N * d - 1, 1),
+                 Fake(B * H * 3, 4), B, H, N, d, scale_rule=fa.FA_FP8_SCALE_POW2)
     t = lambda: Fake(B * H * N * d)
     raises_short("dk", fa.fa_bwd, t(), t(), t(), t(), t(), Fake(B * H * N, 4), t(),
                  Fake(B * H * N * d - 1), t(), B, H, N, d, 0.1, True)
