@@ -230,7 +230,7 @@ __device__ __forceinline__ void lds_barrier() {
 // P, and dV^T += dO^T P; role 1 holds V^T and forms dP = dO V^T, reads the
 // bf16 P its partner left in LDS, forms dS = P (dP - D) and
 // dK^T += Q^T dS.  With one resident operand and one accumulator per wave
-// (256 registers at d = 128 with the deferred products' state; both
+// (~210 registers at d = 128 with the deferred products' state; both
 // operands and accumulators on one wave would need ~350), eight waves -- two
 // per SIMD -- share a 128-key workgroup.  Waves w and w + 4 (one SIMD) form
 // pair w.  Per 32-query block the pair meets at one barrier (P handed over);
