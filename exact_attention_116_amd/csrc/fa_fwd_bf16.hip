@@ -25,7 +25,7 @@
 //    instructions), issued for tile j+1 while tile j is computed; rows past
 //    N read as 0 through the buffer resource's range.  K and V are stored
 //    row-major with the 16-byte chunks of each row XOR-swizzled (K by the
-//    row index mod 16, V by twice the row index mod 4) so that the MFMA
+//    row index mod 16, V by 4 (2 at d = 64) times the row index mod 4) so that the MFMA
 //    operand reads hit distinct LDS banks.  V^T operands are read with the
 //    transposing ds_read_b64_tr_b16: lane j of each 16-lane group points at
 //    one key row and four columns, and lane i receives one column over four
@@ -162,11 +162,19 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   // Direct global -> LDS loads.  One wave instruction fills 1 KB of LDS
   // (lane i -> bytes 16i..16i+15); the 16-byte chunk c of row r sits at
-  // chunk position c ^ (r % NCH) for K and c ^ 2(r % 4) for V, so the MFMA
+  // chunk position c ^ (r % NCH) for K and c ^ VS(r % 4) for V, so the MFMA
   // reads below hit distinct banks.  Each lane's global offset carries the
   // inverse permutation.
   constexpr int RB = D * 2;                      // bytes per row
   constexpr int NCH = RB / 16;                   // chunks per row
+  // V's swizzle step.  A transposing read serves 32 lanes at a time: four
+  // rows (r % 4 = 0..3) times one aligned group of four 16-byte chunks.  At
+  // d = 128 a row is 256 bytes, every bank once, so the four rows' groups
+  // must land on four different groups of chunk positions: XOR by 4(r % 4).
+  // (XOR by 2(r % 4) put rows r and r ^ 1 on the same banks: a two-way
+  // conflict on every V^T read.)  At d = 64 two rows share the banks' width
+  // and 2(r % 4) is conflict-free.
+  constexpr int VS = D == 128 ? 4 : 2;
   constexpr int NI = BC * RB / 1024;             // 1 KB instructions per tile
   constexpr int IPW = NI / NW;                   // per wave, for K and for V each
   static_assert(NI % NW == 0 && NCH >= 8, "direct-load tiling");
@@ -177,7 +185,7 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const int byte = blk * 1024 + lane * 16;
     const int r = byte / RB, p = (byte % RB) / 16;
     gk[x] = (uint32_t)r * RG + (uint32_t)(16 * (p ^ (r % NCH)));
-    gv[x] = (uint32_t)r * RG + (uint32_t)(16 * (p ^ (2 * (r & 3))));
+    gv[x] = (uint32_t)r * RG + (uint32_t)(16 * (p ^ (VS * (r & 3))));
   }
   // key tile j into LDS stage st
   auto load_tile = [&](int j, int st) {
@@ -209,7 +217,7 @@ void fa_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb) {
       const int c = 4 * cb + 2 * dh + ((j16 & 3) >> 1);
-      v_rd[cb] = (uint32_t)(r * RB + 16 * (c ^ (2 * (r & 3))) + 8 * (j16 & 1));
+      v_rd[cb] = (uint32_t)(r * RB + 16 * (c ^ (VS * (r & 3))) + 8 * (j16 & 1));
     }
   }
   int gt = 0;                // tiles computed so far (LDS stage = gt & 1)
