@@ -61,15 +61,15 @@ PEAK_HBM_GBS = 8000.0
 # split-merge kernel's counters to the split kernel's.
 COUNTER_SCALE = {"fetch": 1048576.0 / 524306.0, "write": 1.0}
 TRAFFIC_KIB = {
-    "c3": {"src": ["fa_fwd_bf16.hip"], "fetch_kib": 211485.6, "write_kib": 68608.0,
-           "sha256": "accc1a5b37879305a9d781e6f55e41f204d819c1335a16a5b057084035a8686b"},
-    "c4": {"src": ["fa_decode.hip"], "fetch_kib": 4198852.4, "write_kib": 8778.0,
+    "c3": {"src": ["fa_fwd_bf16.hip"], "fetch_kib": 216148.6, "write_kib": 68608.0,
+           "sha256": "ecdf90041e517b2d5cd99d06309bcf1600c87e194a150bc76296d5954801fa54"},
+    "c4": {"src": ["fa_decode.hip"], "fetch_kib": 4198860.0, "write_kib": 8777.7,
            "sha256": "5e97611a26ac2cfece3c36bca4885bf4a61a66ef052765835b53367d362e873e"},
-    "c5": {"src": ["fa_fwd_fp8.hip"], "fetch_kib": 456000.1, "write_kib": 106499.3,
+    "c5": {"src": ["fa_fwd_fp8.hip"], "fetch_kib": 456066.1, "write_kib": 106499.2,
            "sha256": "f09e1f40ea42b9852f993b74cc5a4067dc42a7715519cab56e494b536cc8d1b0"},
-    "c6": {"src": ["fa_decode_gqa.hip", "fa_decode.hip"], "fetch_kib": 1057845.6, "write_kib": 17679.7,
+    "c6": {"src": ["fa_decode_gqa.hip", "fa_decode.hip"], "fetch_kib": 1057863.5, "write_kib": 17699.4,
            "sha256": "5173b008bb12a55976be3113d7be1d4c27cdcd419827915ad4c16c6113ac15a9"},
-    "c7": {"src": ["fa_decode_gqa.hip", "fa_decode.hip"], "fetch_kib": 135572.8, "write_kib": 8777.9,
+    "c7": {"src": ["fa_decode_gqa.hip", "fa_decode.hip"], "fetch_kib": 135572.7, "write_kib": 8777.7,
            "sha256": "5173b008bb12a55976be3113d7be1d4c27cdcd419827915ad4c16c6113ac15a9"},
 }
 
