@@ -320,6 +320,11 @@ def test_bwd_varlen_rejects(lib, kw, status):
     assert fa.fa_last_error() != ""
     # D takes H * total_q fp32 values: the dense workspace of one batch of total_q rows
     assert fa.fa_bwd_workspace_bytes(1, 4, 100) == 3584   # (448 + 400) * 4 rounded up to 256
+    # two fp32 row arrays, the second 256-byte aligned after the first
+    for B, H, N in ((1, 1, 1), (2, 3, 65), (4, 16, 8192), (1, 32, 14072)):
+        rows = B * H * N
+        nb = fa.fa_bwd_workspace_bytes(B, H, N)
+        assert nb % 256 == 0 and nb >= (-(-rows // 64) * 64 + rows) * 4
 
 
 def test_binding_rejects_host_and_strided_tensors():

@@ -103,12 +103,15 @@ def test_quantize_pow2_scales(gpu_lib, N, rot, d):
         assert np.all(np.abs(a - mid) <= 1e-5 * a) and np.mean(diff) < 1e-2
 
 
-def test_quantize_zero_block(gpu_lib):
+@pytest.mark.parametrize("pow2", [False, True])
+def test_quantize_zero_block(gpu_lib, pow2):
+    """An all-zero block gets scale 1 and zero codes under either scale rule."""
     fa = gpu_lib
     B, H, N, d = 1, 1, 130, 128
     xb = fi.outlier_bf16_tensor(9190, fi.Q_ID, B, H, N, d)
     xb[0, 0, 64:128] = 0
-    codes, scales = quantize(fa, xb, B, H, N, d, fi.rotation_signs(9190, d))
+    codes, scales = quantize(fa, xb, B, H, N, d, fi.rotation_signs(9190, d),
+                             rule=fa.FA_FP8_SCALE_POW2 if pow2 else None)
     assert scales[0, 0, 1].item() == 1.0
     assert torch.all(codes[0, 0, 64:128] == 0)
 
